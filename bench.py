@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of one chunk step of paged top-K chunk attention on one MI355X.
+
+A step is the whole hot path of the OOMB page's method (technical summary,
+section 2) for one attention layer and one chunk: representative vectors of the
+chunk's new pages, chunk-mean-query page scores and top-K per kv-head, the fused
+forward over the selected pages plus the causal chunk, and the fused backward
+that reuses the selection and adds dK/dV in place into the paged fp32 gradient
+pools.  Inputs are seeded synthetic tensors of the Qwen2.5-7B attention shape
+(28 query heads, 4 kv heads, head dim 128, 128-token pages), resident in HBM
+before the timed region; the rep vectors of the prior context are built once,
+untimed.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse-256k]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "chunk attn fwd+bwd tokens/s and MFMA util, Qwen2.5-7B shape, 256K ctx top-K"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def kernel_work(p, name):
+    """Algorithmic work of one launch: (bound, amount, unit).  Attention flops
+    count only visible (query-head row, key) pairs: forward 4*D per pair (QK^T,
+    PV), backward 10*D per pair (QK^T, dO V^T, dV, dK, dQ).  The key-major
+    dK/dV kernel is credited S, dP, dV, dK (8*D); the query-major dQ kernel is
+    credited dQ only (2*D), its S and dP being recomputation."""
+    pairs = p.pairs()
+    eb = 2 if p.dtype == "bf16" else 4
+    if name == "fwd_kernel":
+        return "mfma", 4.0 * p.d * pairs, "flop"
+    if name == "dkdv_kernel":
+        return "mfma", 8.0 * p.d * pairs, "flop"
+    if name == "dq_kernel":
+        return "mfma", 2.0 * p.d * pairs, "flop"
+    if name == "rep_update_kernel":     # the chunk's pages: read ps*D keys, write D floats, per (page, head)
+        return "hbm", p.chunk_pages * p.hkv * (p.ps * p.d * eb + p.d * 4), "byte"
+    if name == "qmean_partial_kernel":  # read Q
+        return "hbm", p.c * p.hq * p.d * eb, "byte"
+    if name == "scores_kernel":         # read the rep rows of the N prior pages, write N*Hkv scores
+        return "hbm", p.n * p.hkv * p.d * 4 + p.n * p.hkv * 4, "byte"
+    if name == "dt_kernel":             # read O and dO, write Dt
+        return "hbm", 2 * p.c * p.hq * p.d * eb + p.c * p.hq * 4, "byte"
+    return "hbm", 0.0, "byte"
+
+
+class HipEvents:
+    """hipEvent_t handles made and read through the process's HIP runtime."""
+
+    def __init__(self, runtime_path, n):
+        self.rt = ctypes.CDLL(runtime_path)
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            self._ok(self.rt.hipEventCreate(ctypes.byref(ev)), "hipEventCreate")
+            self.handles[i] = ev.value
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with hipError {rc}")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        self._ok(self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[a]),
+                                             ctypes.c_void_p(self.handles[b])), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        for h in self.handles:
+            if h:
+                self.rt.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def cpu_baseline(p, seed, x, tokens):
+    """The fp64 oracle, as it stands, on the host cores: the selection over the
+    whole chunk plus forward and backward of `tokens` chunk tokens (all heads),
+    scaled to one chunk step."""
+    import numpy as np
+    import oracle
+    oracle.build()
+    ora = oracle.Oracle()
+    pt = x["page_table"]
+    t0 = time.perf_counter()
+    rep = ora.rep(p, x["k_pool"], pt, 0, p.n)      # rep vectors of the prior context: setup, as on the GPU
+    t_setup = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ora.rep(p, x["k_pool"], pt, p.n, p.chunk_pages)
+    sel = ora.select(p, ora.scores(p, ora.qmean(p, x["q"]), rep))
+    t_sel = time.perf_counter() - t0
+    # rows of tokens spread over the chunk
+    toks = np.linspace(0, p.c - 1, tokens).astype(np.int64)
+    rows = (toks[:, None] * p.hq + np.arange(p.hq)[None, :]).reshape(-1)
+    t0 = time.perf_counter()
+    ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], pt, sel, x["do"], rows=rows)
+    t_rows = time.perf_counter() - t0
+    t_step = t_sel + t_rows * (p.c / tokens)
+    return {"value": p.c / t_step, "unit": "tokens/s", "cores": ora.threads(), "kind": "oracle",
+            "sample": (f"rep vectors of the chunk's pages and selection over the full chunk ({t_sel:.2f} s) + forward and backward (dQ, and dK/dV "
+                       f"of every key) of {tokens} of {p.c} chunk tokens x {p.hq} heads ({t_rows:.2f} s), "
+                       f"scaled to {p.c} tokens; fp64"),
+            "seconds": t_sel + t_rows, "rep_setup_seconds": t_setup}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sparse-256k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="chunk tokens in the oracle's timed sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by kv-head across GPUs by design but no multi-GPU code is built", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_sparse_attention_amd as P
+    from paged_sparse_attention_amd.step import ChunkStep
+
+    seed, p = synth.WORKLOADS[args.workload]
+    print(f"bench: workload {args.workload} {p}", file=sys.stderr, flush=True)
+    x = synth.make_inputs(p, seed)
+    tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+
+    def dev(a, bf=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf else t).cuda()
+
+    bf = p.dtype == "bf16"
+    q, k, v, do = dev(x["q"], bf), dev(x["k_pool"], bf), dev(x["v_pool"], bf), dev(x["do"], bf)
+    pt = dev(x["page_table"])
+    dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    st = ChunkStep(p.hq, p.hkv, p.d, p.ps, p.c, p.n, p.k, p.slots, dtype=p.dtype)
+    st.rep_update(k, pt, 0, p.n)   # rep vectors of the prior context: setup, untimed
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        st.step(q, k, v, pt, do, dk, dv)
+    torch.cuda.synchronize()
+
+    # per-kernel HIP events on the launch stream, recorded by the library around each kernel
+    hip = HipEvents(P.hip_runtimes_loaded()[0], 2 * 16 * args.steps)
+    P.oomb_trace_events(hip.handles)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        st.step(q, k, v, pt, do, dk, dv)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_traced = P.oomb_trace_count()
+    names = [P.oomb_trace_kernel(i) for i in range(max(n_traced, 0))]
+    P.oomb_trace_events(None)
+    if n_traced <= 0:
+        raise RuntimeError(f"kernel tracing recorded nothing (status {n_traced})")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    durations = {}
+    for i, name in enumerate(names):
+        durations.setdefault(name, []).append(hip.elapsed_ms(2 * i, 2 * i + 1))
+    kernels = {n: {"launches": len(v), "avg_ms": statistics.mean(v)} for n, v in durations.items()}
+    print("bench: per-kernel ms " + json.dumps({n: [round(x, 4) for x in v[:4]] for n, v in durations.items()}),
+          file=sys.stderr, flush=True)
+    if not any(kv["avg_ms"] > 0 for kv in kernels.values()):
+        raise RuntimeError("kernel events report zero durations")
+    dominant = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches"])
+    bound, work, unit = kernel_work(p, dominant)
+    avg_s = kernels[dominant]["avg_ms"] / 1e3
+    if bound == "mfma":
+        peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
+        achieved = work / avg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": None, "work_per_launch": work}
+    else:
+        achieved = work / avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "work_per_launch": work}
+    for n, kv in kernels.items():
+        b, w, u = kernel_work(p, n)
+        s = kv["avg_ms"] / 1e3
+        kv["achieved"] = (w / s / 1e12) if b == "mfma" else (w / s / 1e9)
+        kv["unit"] = "TFLOP/s" if b == "mfma" else "GB/s"
+    attn_ms = sum(kernels[n]["avg_ms"] for n in ("fwd_kernel", "dt_kernel", "dkdv_kernel", "dq_kernel")
+                  if n in kernels)
+    attn_flops = 14.0 * p.d * p.pairs()
+    peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    out = {
+        "metric": METRIC,
+        "value": p.c / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "n_q_heads": p.hq, "n_kv_heads": p.hkv, "head_dim": p.d,
+                   "page_size": p.ps, "chunk_len": p.c, "prior_pages": p.n, "prior_tokens": p.n * p.ps,
+                   "top_k": p.k, "visible_pairs": p.pairs(), "seed": seed},
+        "roofline": roof,
+        "attention_mfma_frac": attn_flops / (attn_ms / 1e3) / 1e12 / peak,
+        "attention_ms": attn_ms,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(p, seed, x, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/* oomb.h -- C ABI of the MI355X (gfx950) paged top-K chunk attention library.
+ *
+ * One chunk step of chunk-recurrent attention over a paged KV cache, as the
+ * page "Out of the Memory Barrier: A Highly Memory Efficient Training System
+ * for LLMs with Million-Token Contexts" (OOMB) describes it in its technical
+ * summary, section 2 (Methodology):
+ *   - "Paged Memory Management": the KV cache and its gradients live in
+ *     page-granular buffers (the pools below, addressed through a page table);
+ *     gradients are accumulated into them in place, outside any autograd graph,
+ *     with no concatenated tensors.
+ *   - "Page-level Sparse Attention": in the forward pass a top-K page search
+ *     over per-page representative vectors picks the most relevant key pages;
+ *     the backward pass reuses that choice.
+ *   - "Specialized Kernels": KV-cache operations are kept out of the autograd
+ *     graph.
+ * A chunk of C query tokens attends causally to itself and to the K selected
+ * prior pages of its kv-head.
+ *
+ * Readings taken where the page is silent (the page gives prose only):
+ *   - representative vector of a page = mean of its stored keys, per kv-head;
+ *   - page score = (mean query of the chunk over its C tokens and the query
+ *     heads of the kv-head's group) . (representative vector); one selection per
+ *     (chunk, kv-head); exact score ties go to the lower page index;
+ *   - only the N prior pages are candidates; the chunk's own C/ps pages are
+ *     always attended, causally (chunk token u is visible to query token t iff
+ *     u <= t);
+ *   - query head g reads kv-head g / (Hq / Hkv) (contiguous GQA groups);
+ *   - softmax scale 1/sqrt(D) unless given; the backward holds the selection
+ *     fixed and differentiates with respect to Q, K and V.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked host; the caller owns every
+ *     buffer.  The library never allocates, frees or synchronises; all work is
+ *     enqueued on `stream` (a hipStream_t passed as void*, NULL = the default
+ *     stream) and returns before it runs.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - Element type "T" is the descriptor's dtype (fp32 or bf16); dq, lse, rep,
+ *     scores and the gradient pools are always fp32.
+ *   - Layouts (row-major):
+ *       q, o, dO          T     [C][Hq][D]
+ *       k_pool, v_pool    T     [n_slots][Hkv][ps][D]
+ *       dk_pool, dv_pool  fp32  [n_slots][Hkv][ps][D]
+ *       page_table        int32 [N + C/ps]      logical page -> physical slot;
+ *                                               the chunk's tokens are logical
+ *                                               pages N .. N + C/ps - 1
+ *       rep               fp32  [rep_capacity][Hkv][D]   by logical page
+ *       sel               int32 [Hkv][K_eff]    logical pages, ascending,
+ *                                               K_eff = min(top_k, N)
+ *       lse               fp32  [Hq][C]         natural log, scale included
+ *   - Errors: every check on the host descriptor, sizes and pointers runs
+ *     before any HIP call; on failure the call returns a negative status,
+ *     launches nothing and writes nothing.  Device-resident contents
+ *     (page_table, sel) are trusted: entries out of range are undefined
+ *     behaviour.  A launch error maps to OOMB_ERR_LAUNCH; faults inside a
+ *     kernel surface at the caller's next synchronisation.  No C++ exception
+ *     crosses this interface.
+ *   - Calls on one stream run in order; calls on different streams that write
+ *     the same buffer race.
+ */
+#ifndef OOMB_H
+#define OOMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OOMB_ABI_VERSION 1
+
+typedef enum { OOMB_F32 = 0, OOMB_BF16 = 1 } oomb_dtype;
+
+typedef enum {
+  OOMB_OK = 0,
+  OOMB_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  OOMB_ERR_BAD_SHAPE = -2,   /* inconsistent sizes (e.g. Hq % Hkv != 0, C % ps != 0) */
+  OOMB_ERR_UNSUPPORTED = -3, /* valid but not built (D not in {64,128}, ps not in {16,32,64,128}, ...) */
+  OOMB_ERR_BAD_DTYPE = -4,   /* dtype not an oomb_dtype */
+  OOMB_ERR_MISALIGNED = -5,  /* a device pointer is not 16-byte aligned */
+  OOMB_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
+  OOMB_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
+} oomb_status;
+
+/* Host-side descriptor of one chunk step. */
+typedef struct {
+  int32_t n_q_heads;      /* Hq > 0 */
+  int32_t n_kv_heads;     /* Hkv > 0, Hq % Hkv == 0, Hkv * D <= 1024 */
+  int32_t head_dim;       /* D in {64, 128} */
+  int32_t page_size;      /* ps in {16, 32, 64, 128} */
+  int32_t chunk_len;      /* C > 0, C % ps == 0, C * Hq < 2^30 */
+  int32_t n_prior_pages;  /* N >= 0: candidate logical pages 0 .. N-1 */
+  int32_t top_k;          /* >= 0; K_eff = min(top_k, N); top_k >= N attends every prior page;
+                             K_eff * ps + C < 2^30 */
+  int32_t n_slots;        /* physical pages in each pool, >= N + C/ps */
+  int32_t rep_capacity;   /* rows of the rep table, >= N + C/ps */
+  int32_t dtype;          /* oomb_dtype of q, k/v pools, o, dO */
+  float softmax_scale;    /* > 0, or 0 for 1/sqrt(D) */
+} oomb_desc;
+
+/* Representative-vector update (OOMB, section 2, "Page-level Sparse Attention":
+ * pages are ranked by representative vectors; reading: the mean of the page's
+ * keys).  For i < n_pages and every kv-head h:
+ *     rep[first_page + i][h][:] = (1/ps) * sum_r k_pool[page_table[first_page + i]][h][r][:]
+ * accumulated in fp32.  Needs 0 <= first_page, first_page + n_pages <= N + C/ps
+ * and <= rep_capacity.  n_pages == 0 is a no-op.  Other rep rows are untouched. */
+int oomb_rep_update(const oomb_desc* desc, const void* k_pool, const int32_t* page_table,
+                    int32_t first_page, int32_t n_pages, float* rep, void* stream);
+
+/* Bytes of device workspace oomb_select_topk needs (0 if desc is invalid). */
+size_t oomb_select_workspace_bytes(const oomb_desc* desc);
+
+/* Top-K page selection (OOMB, section 2, "Page-level Sparse Attention": a
+ * top-K page search over representative vectors, made in the forward pass).
+ *   qbar[h]   = mean of q[t][g] over t < C and the heads g of group h (fp32)
+ *   score[h][n] = qbar[h] . rep[n][h]                    for n < N
+ *   sel[h]    = the K_eff pages of highest score, exact ties to the lower page,
+ *               written in ascending page order; top_k >= N gives 0..N-1.
+ * scores_out (fp32 [Hkv][N]) receives the scores when not NULL.
+ * Deterministic: no atomics; repeated calls give identical bits. */
+int oomb_select_topk(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
+                     float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused forward (OOMB, section 2: attention over the selected pages plus the
+ * local chunk).  For chunk token t and query head g, h = g / (Hq/Hkv), the key
+ * set J is every token of the pages sel[h][:] and chunk tokens u <= t:
+ *   s_j = scale * q[t][g] . k_j,  lse[g][t] = ln sum_j exp(s_j),
+ *   o[t][g] = sum_j exp(s_j - lse[g][t]) v_j.
+ * bf16: q.k and p.v on bf16 MFMA with fp32 accumulation; p rounded to bf16.
+ * o and lse are overwritten. */
+int oomb_attn_fwd(const oomb_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* page_table, const int32_t* sel, void* o, float* lse, void* stream);
+
+/* Bytes of device workspace oomb_attn_bwd needs (0 if desc is invalid). */
+size_t oomb_bwd_workspace_bytes(const oomb_desc* desc);
+
+/* Fused backward (OOMB, section 2, "Paged Memory Management": gradients of the
+ * KV cache are accumulated in place into paged buffers; "Page-level Sparse
+ * Attention": the forward's page choice is reused).  With the same J and the
+ * forward's o and lse:
+ *   p_j = exp(s_j - lse),  Dt = dO . o,  ds_j = p_j (dO . v_j - Dt)
+ *   dq[t][g]            = scale * sum_j ds_j k_j                  (overwritten)
+ *   dk_pool[slot(j)]   += scale * sum over rows seeing j of ds_j q
+ *   dv_pool[slot(j)]   += sum over rows seeing j of p_j dO
+ * Only the slots of the selected pages and of the chunk's pages change; every
+ * other byte of the gradient pools is left as it was.  Deterministic (no
+ * atomics).  workspace: oomb_bwd_workspace_bytes(desc) bytes. */
+int oomb_attn_bwd(const oomb_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* page_table, const int32_t* sel, const void* o, const float* lse,
+                  const void* dO, float* dq, float* dk_pool, float* dv_pool, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (host). */
+const char* oomb_status_string(int status);
+
+/* OOMB_ABI_VERSION of the built library. */
+int oomb_abi_version(void);
+
+/* Kernel tracing, for profiling (host).  `events` holds `capacity` hipEvent_t
+ * handles that the caller created; while set, the i-th kernel launched by the
+ * entry points above (counting from this call) records events[2i] on its
+ * stream just before it and events[2i+1] just after it, for 2i+1 < capacity;
+ * later launches record nothing.  events == NULL switches tracing off.
+ * Returns OOMB_ERR_BAD_SHAPE for capacity < 0 or a non-NULL list of capacity 0.
+ * Process-wide state: not for concurrent use from several host threads. */
+int oomb_trace_events(void* const* events, int capacity);
+
+/* Launches recorded since the last oomb_trace_events call, or minus the
+ * hipError_t of the first event record that failed. */
+int oomb_trace_count(void);
+
+/* Static name of the kernel of recorded launch i, or NULL if i is out of range. */
+const char* oomb_trace_kernel(int i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OOMB_H */

@@ -73,9 +73,14 @@ class Oracle:
         L.ora_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp]
         L.ora_bwd.restype = None
         L.ora_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp]
+        L.ora_threads.restype = ctypes.c_int
+        L.ora_threads.argtypes = []
         L.ora_key_offset.restype = ctypes.c_int64
         L.ora_key_offset.argtypes = [P, vp, vp, ctypes.c_int32, ctypes.c_int64]
         self.L = L
+
+    def threads(self) -> int:
+        return self.L.ora_threads()
 
     @staticmethod
     def shape(p, dtype: str | None = None) -> _Shape:

@@ -37,6 +37,17 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int ora_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 static double widen(const void* base, int32_t dtype, int64_t i) {
   if (dtype == ORA_F64) return ((const double*)base)[i];

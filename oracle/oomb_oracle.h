@@ -47,6 +47,9 @@ typedef struct {
   double scale;         /* softmax scale; <= 0 selects 1/sqrt(d) */
 } ora_shape;
 
+/* Host threads the parallel loops use (OpenMP). */
+int ora_threads(void);
+
 /* Number of selected pages per kv-head, min(k, n). */
 int32_t ora_keff(const ora_shape* s);
 /* Keys in J(h): K_eff*ps + C. */

@@ -1,0 +1,166 @@
+"""Python binding of liboomb.so, the gfx950 paged top-K chunk attention library.
+
+Argument marshalling only: each function below has the name of the C entry
+point it calls (declared in include/oomb.h), turns torch tensors into device
+pointers and the current torch stream into a hipStream_t, and raises OombError
+on a negative status.  Every step of the computation runs in the HIP kernels of
+liboomb.so; there is no other code path.  Importing this module fails if the
+library has not been built (python -m paged_sparse_attention_amd.build).
+
+Method: page "Out of the Memory Barrier" (OOMB), technical summary, section 2
+("Paged Memory Management", "Page-level Sparse Attention", "Specialized
+Kernels").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so liboomb.so binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboomb.so")
+
+OOMB_F32, OOMB_BF16 = 0, 1
+DTYPE_CODES = {"f32": OOMB_F32, "bf16": OOMB_BF16, torch.float32: OOMB_F32, torch.bfloat16: OOMB_BF16}
+ABI_VERSION = 1
+
+
+class OombError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class oomb_desc(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("chunk_len", ctypes.c_int32), ("n_prior_pages", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("rep_capacity", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+def make_desc(n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_prior_pages, top_k, n_slots,
+              rep_capacity=None, dtype="bf16", softmax_scale=0.0) -> oomb_desc:
+    pages = n_prior_pages + chunk_len // page_size
+    return oomb_desc(n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_prior_pages, top_k, n_slots,
+                     pages if rep_capacity is None else rep_capacity, DTYPE_CODES[dtype], softmax_scale)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_sparse_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(oomb_desc)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "oomb_rep_update": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp]),
+        "oomb_select_workspace_bytes": (sz, [P]),
+        "oomb_select_topk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "oomb_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "oomb_bwd_workspace_bytes": (sz, [P]),
+        "oomb_attn_bwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "oomb_abi_version": (ctypes.c_int, []),
+        "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
+        "oomb_trace_count": (ctypes.c_int, []),
+        "oomb_trace_kernel": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype, fn.argtypes = res, args
+    if L.oomb_abi_version() != ABI_VERSION:
+        raise ImportError(f"liboomb.so ABI {L.oomb_abi_version()} != {ABI_VERSION}")
+    return L
+
+
+_L = _load()
+
+
+def hip_runtimes_loaded() -> list[str]:
+    """Paths of every libamdhip64 mapped into this process (one is expected)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(line.split()[-1])
+    return sorted(paths)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    raise TypeError(f"expected a tensor, an int address or None, got {type(x)}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise OombError(status, _L.oomb_status_string(status).decode())
+
+
+def oomb_status_string(status: int) -> str:
+    return _L.oomb_status_string(status).decode()
+
+
+def oomb_abi_version() -> int:
+    return _L.oomb_abi_version()
+
+
+def oomb_rep_update(desc, k_pool, page_table, first_page, n_pages, rep, stream=None):
+    _check(_L.oomb_rep_update(ctypes.byref(desc), _ptr(k_pool), _ptr(page_table), first_page, n_pages,
+                              _ptr(rep), _stream(stream)))
+
+
+def oomb_select_workspace_bytes(desc) -> int:
+    return _L.oomb_select_workspace_bytes(ctypes.byref(desc))
+
+
+def oomb_select_topk(desc, q, rep, sel, scores_out, workspace, workspace_bytes=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(_L.oomb_select_topk(ctypes.byref(desc), _ptr(q), _ptr(rep), _ptr(sel), _ptr(scores_out),
+                               _ptr(workspace), nbytes, _stream(stream)))
+
+
+def oomb_attn_fwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, stream=None):
+    _check(_L.oomb_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                            _ptr(sel), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def oomb_bwd_workspace_bytes(desc) -> int:
+    return _L.oomb_bwd_workspace_bytes(ctypes.byref(desc))
+
+
+def oomb_attn_bwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, dO, dq, dk_pool, dv_pool, workspace,
+                  workspace_bytes=None, stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(_L.oomb_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
+                            _ptr(sel), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk_pool), _ptr(dv_pool),
+                            _ptr(workspace), nbytes, _stream(stream)))
+
+
+def oomb_trace_events(events, capacity=None):
+    """Start tracing into a ctypes array of hipEvent_t handles (None stops it)."""
+    if events is None:
+        _check(_L.oomb_trace_events(None, 0))
+        return
+    _check(_L.oomb_trace_events(ctypes.cast(events, ctypes.c_void_p), len(events) if capacity is None else capacity))
+
+
+def oomb_trace_count() -> int:
+    return _L.oomb_trace_count()
+
+
+def oomb_trace_kernel(i: int):
+    name = _L.oomb_trace_kernel(i)
+    return name.decode() if name is not None else None

@@ -1,0 +1,184 @@
+// abi.hip -- the extern "C" entry points of include/oomb.h: validate the
+// descriptor, sizes and pointers on the host (before any HIP call), then
+// enqueue the kernels on the caller's stream.  Nothing is allocated, freed or
+// synchronised here.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "oomb.h"
+#include "trace.h"
+
+#define OOMB_API extern "C" __attribute__((visibility("default")))
+
+namespace oomb {
+TraceState& trace_state() {
+  static TraceState t;
+  return t;
+}
+}  // namespace oomb
+
+namespace {
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+int log2_exact(int v) {
+  for (int b = 0; b < 31; ++b)
+    if (v == (1 << b)) return b;
+  return -1;
+}
+
+int validate(const oomb_desc* d, oomb::Shape* s) {
+  if (!d) return OOMB_ERR_NULL_PTR;
+  if (d->dtype != OOMB_F32 && d->dtype != OOMB_BF16) return OOMB_ERR_BAD_DTYPE;
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads != 0) return OOMB_ERR_BAD_SHAPE;
+  if (d->head_dim <= 0 || d->page_size <= 0 || d->chunk_len <= 0) return OOMB_ERR_BAD_SHAPE;
+  if (d->n_prior_pages < 0 || d->top_k < 0 || d->n_slots <= 0 || d->rep_capacity < 0) return OOMB_ERR_BAD_SHAPE;
+  if (d->chunk_len % d->page_size != 0) return OOMB_ERR_BAD_SHAPE;
+  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return OOMB_ERR_BAD_SHAPE;
+  const int64_t pages_total = (int64_t)d->n_prior_pages + d->chunk_len / d->page_size;
+  if (d->n_slots < pages_total || d->rep_capacity < pages_total) return OOMB_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return OOMB_ERR_UNSUPPORTED;
+  const int ps_log2 = log2_exact(d->page_size);
+  if (ps_log2 < 4 || ps_log2 > 7) return OOMB_ERR_UNSUPPORTED;
+  if ((int64_t)d->n_kv_heads * d->head_dim > 1024) return OOMB_ERR_UNSUPPORTED;
+  const int64_t G = d->n_q_heads / d->n_kv_heads;
+  const int64_t keff = d->top_k < d->n_prior_pages ? d->top_k : d->n_prior_pages;
+  // 32-bit row and key indices inside the kernels
+  if ((int64_t)d->chunk_len * G >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
+  if (keff * d->page_size + d->chunk_len >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
+  if ((int64_t)d->chunk_len * d->n_q_heads >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
+  s->hq = d->n_q_heads;
+  s->hkv = d->n_kv_heads;
+  s->d = d->head_dim;
+  s->ps = d->page_size;
+  s->ps_log2 = ps_log2;
+  s->c = d->chunk_len;
+  s->n = d->n_prior_pages;
+  s->keff = (int)keff;
+  s->n_slots = d->n_slots;
+  s->rep_cap = d->rep_capacity;
+  s->bf16 = d->dtype == OOMB_BF16;
+  s->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  return OOMB_OK;
+}
+
+// Every pointer non-NULL and 16-byte aligned.
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return OOMB_ERR_NULL_PTR;
+  for (const void* p : ps)
+    if (misaligned(p)) return OOMB_ERR_MISALIGNED;
+  return OOMB_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? OOMB_OK : OOMB_ERR_LAUNCH; }
+
+}  // namespace
+
+OOMB_API int oomb_rep_update(const oomb_desc* desc, const void* k_pool, const int32_t* page_table,
+                             int32_t first_page, int32_t n_pages, float* rep, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({k_pool, page_table, rep}))) return rc;
+  const int64_t pages_total = (int64_t)s.n + s.c / s.ps;
+  if (first_page < 0 || n_pages < 0 || (int64_t)first_page + n_pages > pages_total ||
+      (int64_t)first_page + n_pages > s.rep_cap)
+    return OOMB_ERR_BAD_SHAPE;
+  if (n_pages == 0) return OOMB_OK;
+  (void)hipGetLastError();
+  return launched(oomb::launch_rep_update(s, k_pool, page_table, first_page, n_pages, rep, (hipStream_t)stream));
+}
+
+OOMB_API size_t oomb_select_workspace_bytes(const oomb_desc* desc) {
+  oomb::Shape s;
+  if (validate(desc, &s)) return 0;
+  return oomb::select_plan(s).bytes;
+}
+
+OOMB_API int oomb_select_topk(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
+                              float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, rep}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  if (scores_out && misaligned(scores_out)) return OOMB_ERR_MISALIGNED;
+  const oomb::SelectPlan p = oomb::select_plan(s);
+  if (!workspace || workspace_bytes < p.bytes) return OOMB_ERR_WORKSPACE;
+  if (misaligned(workspace)) return OOMB_ERR_MISALIGNED;
+  if (s.n == 0) return OOMB_OK;  // no candidate pages: nothing to score or select
+  (void)hipGetLastError();
+  return launched(oomb::launch_select(s, q, rep, sel, scores_out, workspace, (hipStream_t)stream));
+}
+
+OOMB_API int oomb_attn_fwd(const oomb_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* sel, void* o, float* lse, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, k_pool, v_pool, page_table, o, lse}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  (void)hipGetLastError();
+  return launched(oomb::launch_fwd(s, q, k_pool, v_pool, page_table, sel, o, lse, (hipStream_t)stream));
+}
+
+OOMB_API size_t oomb_bwd_workspace_bytes(const oomb_desc* desc) {
+  oomb::Shape s;
+  if (validate(desc, &s)) return 0;
+  return oomb::bwd_plan(s).bytes;
+}
+
+OOMB_API int oomb_attn_bwd(const oomb_desc* desc, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* page_table, const int32_t* sel, const void* o, const float* lse,
+                           const void* dO, float* dq, float* dk_pool, float* dv_pool, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, k_pool, v_pool, page_table, o, lse, dO, dq, dk_pool, dv_pool}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  const oomb::BwdPlan p = oomb::bwd_plan(s);
+  if (!workspace || workspace_bytes < p.bytes) return OOMB_ERR_WORKSPACE;
+  if (misaligned(workspace)) return OOMB_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  return launched(oomb::launch_bwd(s, q, k_pool, v_pool, page_table, sel, o, lse, dO, dq, dk_pool, dv_pool,
+                                   workspace, (hipStream_t)stream));
+}
+
+OOMB_API const char* oomb_status_string(int status) {
+  switch (status) {
+    case OOMB_OK: return "ok";
+    case OOMB_ERR_NULL_PTR: return "a required pointer is NULL";
+    case OOMB_ERR_BAD_SHAPE: return "inconsistent sizes in the descriptor or arguments";
+    case OOMB_ERR_UNSUPPORTED: return "shape not supported by the built kernels";
+    case OOMB_ERR_BAD_DTYPE: return "dtype is not an oomb_dtype";
+    case OOMB_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
+    case OOMB_ERR_WORKSPACE: return "workspace missing or too small";
+    case OOMB_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+OOMB_API int oomb_abi_version(void) { return OOMB_ABI_VERSION; }
+
+OOMB_API int oomb_trace_events(void* const* events, int capacity) {
+  if (capacity < 0 || (events && capacity == 0)) return OOMB_ERR_BAD_SHAPE;
+  oomb::TraceState& t = oomb::trace_state();
+  t.events = events;
+  t.capacity = events ? capacity : 0;
+  t.count = 0;
+  t.error = 0;
+  return OOMB_OK;
+}
+
+OOMB_API int oomb_trace_count(void) {
+  const oomb::TraceState& t = oomb::trace_state();
+  return t.error ? -t.error : t.count;
+}
+
+OOMB_API const char* oomb_trace_kernel(int i) {
+  const oomb::TraceState& t = oomb::trace_state();
+  return (i >= 0 && i < t.count) ? t.names[i] : nullptr;
+}

@@ -1,0 +1,57 @@
+// launch.h -- host-side plan of one chunk step and the kernel launchers behind
+// the C ABI (include/oomb.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace oomb {
+
+// A validated descriptor.
+struct Shape {
+  int hq, hkv, d, ps, ps_log2, c, n, keff, n_slots, rep_cap;
+  bool bf16;
+  float scale;  // resolved softmax scale
+};
+
+inline Geo make_geo(const Shape& s) {
+  Geo g;
+  g.hq = s.hq;
+  g.hkv = s.hkv;
+  g.G = s.hq / s.hkv;
+  g.c = s.c;
+  g.n = s.n;
+  g.keff = s.keff;
+  g.ps_log2 = s.ps_log2;
+  g.n_slots = s.n_slots;
+  g.scale = s.scale;
+  return g;
+}
+
+constexpr int kQmeanBlocks = 128;  // token blocks of the chunk-mean-query reduction
+
+struct SelectPlan {
+  int tpb, nblk;                                   // tokens per block, blocks
+  size_t off_partial, off_qbar, off_scores, bytes;  // workspace layout
+};
+SelectPlan select_plan(const Shape& s);
+
+struct BwdPlan {
+  size_t off_dt, bytes;  // Dt = rowsum(dO * O) per (head, token), fp32 [Hq][C]
+};
+BwdPlan bwd_plan(const Shape& s);
+
+hipError_t launch_rep_update(const Shape& s, const void* k_pool, const int32_t* pt, int first, int count,
+                             float* rep, hipStream_t st);
+hipError_t launch_select(const Shape& s, const void* q, const float* rep, int32_t* sel, float* scores_out,
+                         void* ws, hipStream_t st);
+hipError_t launch_fwd(const Shape& s, const void* q, const void* k_pool, const void* v_pool, const int32_t* pt,
+                      const int32_t* sel, void* o, float* lse, hipStream_t st);
+hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const void* v_pool, const int32_t* pt,
+                      const int32_t* sel, const void* o, const float* lse, const void* dout, float* dq,
+                      float* dk_pool, float* dv_pool, void* ws, hipStream_t st);
+
+}  // namespace oomb

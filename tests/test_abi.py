@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/oomb.h declares, and rejects bad descriptors, pointers and workspaces
+with the documented status codes before any HIP call (the pointers below are
+fake addresses; every case fails validation, so nothing is launched)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_sparse_attention_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oomb.h")
+
+OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+A = 0x10000        # a fake, 16-byte aligned device address
+B = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oomb_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"oomb_rep_update", "oomb_select_topk", "oomb_attn_fwd", "oomb_attn_bwd"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    # nothing else leaks out of the library
+    assert {e for e in exported if e.startswith("oomb")} == set(names)
+
+
+def test_version_and_status_strings():
+    assert P.oomb_abi_version() == P.ABI_VERSION == 1
+    for code in (OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH):
+        assert P.oomb_status_string(code) and P.oomb_status_string(code) != "unknown status"
+    assert P.oomb_status_string(-99) == "unknown status"
+
+
+def test_single_hip_runtime():
+    assert len(P.hip_runtimes_loaded()) == 1
+
+
+def good(**kw):
+    base = dict(n_q_heads=28, n_kv_heads=4, head_dim=128, page_size=128, chunk_len=4096, n_prior_pages=2048,
+                top_k=64, n_slots=2080)
+    base.update(kw)
+    return P.make_desc(**base)
+
+
+def fwd(d, **ptrs):
+    p = dict(q=A, k=A, v=A, pt=A, sel=A, o=A, lse=A)
+    p.update(ptrs)
+    return P._L.oomb_attn_fwd(P.ctypes.byref(d), p["q"], p["k"], p["v"], p["pt"], p["sel"], p["o"], p["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=28, n_kv_heads=5), BAD_SHAPE),
+    (dict(n_q_heads=0), BAD_SHAPE),
+    (dict(chunk_len=4000), BAD_SHAPE),
+    (dict(chunk_len=0), BAD_SHAPE),
+    (dict(n_slots=2079), BAD_SHAPE),
+    (dict(rep_capacity=2000), BAD_SHAPE),
+    (dict(n_prior_pages=-1), BAD_SHAPE),
+    (dict(top_k=-3), BAD_SHAPE),
+    (dict(softmax_scale=-1.0), BAD_SHAPE),
+    (dict(softmax_scale=float("nan")), BAD_SHAPE),
+    (dict(head_dim=96), UNSUPPORTED),
+    (dict(page_size=256, chunk_len=4096), UNSUPPORTED),
+    (dict(page_size=8, chunk_len=4096, n_slots=3000), UNSUPPORTED),
+    (dict(n_kv_heads=28, n_q_heads=28), UNSUPPORTED),   # Hkv * D > 1024
+])
+def test_bad_descriptor(kw, code):
+    assert fwd(good(**kw)) == code
+
+
+def test_bad_dtype_and_null_desc():
+    d = good()
+    d.dtype = 7
+    assert fwd(d) == BAD_DTYPE
+    assert P._L.oomb_attn_fwd(None, A, A, A, A, A, A, A, None) == NULL_PTR
+    assert P.oomb_select_workspace_bytes(d) == 0 and P.oomb_bwd_workspace_bytes(d) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "pt", "sel", "o", "lse"])
+def test_null_and_misaligned_pointers(name):
+    d = good(n_slots=0)  # also invalid: must report the descriptor first
+    assert fwd(d, **{name: None}) == BAD_SHAPE
+    # the descriptor is made valid but the pointer is NULL / misaligned: rejected before launch
+    assert fwd(good(), **{name: None}) == NULL_PTR
+    assert fwd(good(), **{name: A + 4}) == MISALIGNED
+
+
+def test_sel_may_be_null_without_selection():
+    # K_eff = 0 needs no sel pointer; a NULL q must still be caught
+    assert fwd(good(top_k=0), sel=None, q=None) == NULL_PTR
+    assert fwd(good(n_prior_pages=0, n_slots=32), sel=None, lse=A + 8) == MISALIGNED
+
+
+def test_workspaces():
+    d = good()
+    ws = P.oomb_select_workspace_bytes(d)
+    wb = P.oomb_bwd_workspace_bytes(d)
+    assert ws > 0 and wb >= 28 * 4096 * 4
+    L = P._L
+    r = L.oomb_select_topk(P.ctypes.byref(d), A, A, A, None, A, ws - 1, None)
+    assert r == WORKSPACE
+    assert L.oomb_select_topk(P.ctypes.byref(d), A, A, A, None, None, ws, None) == WORKSPACE
+    assert L.oomb_select_topk(P.ctypes.byref(d), A, A, A, None, A + 4, ws, None) == MISALIGNED
+    args = [A] * 11
+    assert L.oomb_attn_bwd(P.ctypes.byref(d), *args, A, wb - 1, None) == WORKSPACE
+    assert L.oomb_attn_bwd(P.ctypes.byref(d), *args, None, wb, None) == WORKSPACE
+    args[8] = None  # dq
+    assert L.oomb_attn_bwd(P.ctypes.byref(d), *args, A, wb, None) == NULL_PTR
+
+
+def test_rep_update_ranges():
+    d = good()
+    L = P._L
+    total = 2048 + 4096 // 128
+    assert L.oomb_rep_update(P.ctypes.byref(d), A, A, -1, 4, A, None) == BAD_SHAPE
+    assert L.oomb_rep_update(P.ctypes.byref(d), A, A, 0, total + 1, A, None) == BAD_SHAPE
+    assert L.oomb_rep_update(P.ctypes.byref(d), A, A, total - 3, 4, A, None) == BAD_SHAPE
+    assert L.oomb_rep_update(P.ctypes.byref(d), A, A, 0, -1, A, None) == BAD_SHAPE
+    assert L.oomb_rep_update(P.ctypes.byref(d), None, A, 0, 4, A, None) == NULL_PTR
+    assert L.oomb_rep_update(P.ctypes.byref(d), A, A, 0, 4, A + 2, None) == MISALIGNED
+
+
+def test_binding_raises():
+    with pytest.raises(P.OombError) as e:
+        P.oomb_attn_fwd(good(head_dim=80), A, A, A, A, A, A, A, stream=0)
+    assert e.value.status == UNSUPPORTED

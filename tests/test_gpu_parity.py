@@ -1,0 +1,126 @@
+"""HIP path against the fp64 oracle on an MI355X, through the C ABI.
+
+Small problems: every output element by element (they span several tiles and
+have ragged tails).  Full-size workloads: exact rep vectors and selection,
+sampled rows, the last chunk keys, invariants, and every key's dK/dV under a dO
+supported on sampled rows.  Bars: see parity.py."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import Problem, WORKLOADS
+import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny-fp32": (1, WORKLOADS["tiny-fp32"][1]),
+    "gqa7-ps64-ragged": (21, Problem(hq=28, hkv=4, d=128, ps=64, c=320, n=24, k=6)),
+    "qwen-ps128": (22, Problem(hq=28, hkv=4, d=128, ps=128, c=256, n=12, k=4)),
+    "dense-k-ge-n": (23, Problem(hq=8, hkv=2, d=128, ps=64, c=128, n=6, k=10)),
+    "k0-local-only": (24, Problem(hq=4, hkv=1, d=128, ps=16, c=48, n=5, k=0)),
+    "n0-no-prior": (25, Problem(hq=4, hkv=2, d=64, ps=32, c=96, n=0, k=4)),
+    "mha-fp32-d128": (26, Problem(hq=2, hkv=2, d=128, ps=32, c=64, n=9, k=3, dtype="f32")),
+    "one-page-chunk": (27, Problem(hq=12, hkv=3, d=64, ps=16, c=16, n=40, k=7)),
+    "extra-slots": (28, Problem(hq=6, hkv=2, d=64, ps=32, c=64, n=10, k=4, n_slots=30)),
+    "scale-override-fp32": (29, Problem(hq=4, hkv=2, d=64, ps=16, c=32, n=8, k=3, dtype="f32", scale=0.05)),
+    "d64-bf16-g7": (30, Problem(hq=14, hkv=2, d=64, ps=16, c=112, n=31, k=9)),
+}
+
+FULL = ["dense-32k", "sparse-256k", "sparse-1m", "sparse-4m"]
+
+REPORT_DIR = os.environ.get("OOMB_PARITY_REPORT_DIR")
+
+
+def _save(name, report):
+    if REPORT_DIR:
+        os.makedirs(REPORT_DIR, exist_ok=True)
+        with open(os.path.join(REPORT_DIR, f"parity_{name}.json"), "w") as f:
+            json.dump(report, f, indent=1, default=float)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
+    import paged_sparse_attention_amd as P
+    assert len(P.hip_runtimes_loaded()) == 1, P.hip_runtimes_loaded()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_elementwise(ora, name):
+    seed, p = SMALL[name]
+    H.say(f"case {name}: {p}")
+    report, *_ = H.run_full(p, seed, ora)
+    H.say(f"  {json.dumps(report, default=float)}")
+    _save(name, report)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(ora, name):
+    seed, p = WORKLOADS[name]
+    H.say(f"workload {name}: {p}")
+    report = H.run_sampled(p, seed, ora)
+    H.say(f"  {json.dumps(report, default=float)}")
+    _save(name, report)
+    torch.cuda.empty_cache()
+
+
+def test_deterministic_and_stream(ora):
+    """Repeated runs give identical bits; a non-default stream gives the same bits."""
+    seed, p = SMALL["gqa7-ps64-ragged"]
+    x = synth.make_inputs(p, seed)
+    outs = []
+    for use_stream in (False, False, True):
+        d = H.Device(p, x, canary_seed=seed)
+        st = H.make_step(p)
+        s = torch.cuda.Stream() if use_stream else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            st.rep_update(d.k, d.pt, 0, p.n + p.chunk_pages)
+            st.select(d.q)
+            st.fwd(d.q, d.k, d.v, d.pt)
+            st.bwd(d.q, d.k, d.v, d.pt, d.do, d.dk, d.dv)
+        s.synchronize()
+        outs.append([t.cpu().clone() for t in (st.rep, st.scores, st.sel, st.o, st.lse, st.dq, d.dk, d.dv)])
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    for a, b in zip(outs[0], outs[2]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_rep_update_range_only(ora):
+    """oomb_rep_update writes exactly rows [first, first + count) of the rep table."""
+    seed, p = SMALL["qwen-ps128"]
+    x = synth.make_inputs(p, seed)
+    d = H.Device(p, x)
+    st = H.make_step(p)
+    st.rep.fill_(7.0)
+    first, count = p.n - 3, 3 + p.chunk_pages
+    st.rep_update(d.k, d.pt, first, count)
+    torch.cuda.synchronize()
+    rep = st.rep.cpu().numpy()
+    assert np.all(rep[:first] == 7.0)
+    want = ora.rep(p, x["k_pool"], x["page_table"], first, count)
+    assert np.max(np.abs(rep[first:first + count] - want)) <= 1e-5
+
+
+def test_bwd_accumulates(ora):
+    """Two backward calls add twice the gradient to the pools (in-place accumulation)."""
+    seed, p = SMALL["qwen-ps128"]
+    x = synth.make_inputs(p, seed)
+    d = H.Device(p, x)
+    st = H.make_step(p)
+    st.rep_update(d.k, d.pt, 0, p.n + p.chunk_pages)
+    st.select(d.q)
+    st.fwd(d.q, d.k, d.v, d.pt)
+    st.bwd(d.q, d.k, d.v, d.pt, d.do, d.dk, d.dv)
+    once_k, once_v = d.dk.clone() - 0.5, d.dv.clone() + 0.25
+    st.bwd(d.q, d.k, d.v, d.pt, d.do, d.dk, d.dv)
+    torch.cuda.synchronize()
+    twice_k, twice_v = d.dk - 0.5, d.dv + 0.25
+    assert torch.allclose(twice_k, 2 * once_k, atol=1e-6, rtol=1e-5)
+    assert torch.allclose(twice_v, 2 * once_v, atol=1e-6, rtol=1e-5)
