@@ -6,15 +6,17 @@
 // from its pages ("Paged Memory Management").  The forward saves O and the
 // log-sum-exp for the backward.
 //
-// Work split: one workgroup = one kv-head h and 128 query rows of that head's
+// Work split: one workgroup = one kv-head h and 256 query rows of that head's
 // C*G rows (row r = token r / G, query head h*G + r % G), so every K/V tile
-// staged in LDS serves all G query heads of the group.  Four waves own 32 rows
-// each.  Scores are computed transposed, S^T = K Q^T on bf16 MFMA 32x32x16
-// (fp32 MFMA 32x32x2 for fp32 inputs): a lane then owns one query row, and the
-// online-softmax max and sum are in-lane plus one cross-half exchange.  P^T
-// (rounded to the input type) is reused in registers as the B operand of
-// O^T += V^T P^T, whose A operand comes from V staged transposed in operand
-// order.
+// staged in LDS serves all G query heads of the group.  Eight waves own 32 rows
+// each (two waves per SIMD, so one wave's softmax overlaps another's MFMA).
+// Scores are computed transposed, S^T = K Q^T on bf16 MFMA 32x32x16 (fp32
+// MFMA 32x32x2 for fp32 inputs): a lane owns one query row, and the softmax
+// max and sum are in-lane plus one cross-half exchange.  P^T (rounded to the
+// input type) is the B operand of O^T += V^T P^T, whose A operand is read
+// transposed from the row-major V tile.  K/V tiles of 64 keys are
+// double-buffered: the next tile's global loads are in flight while the current
+// one is used, with one barrier per tile.
 #include "common.h"
 #include "launch.h"
 #include "tiles.h"
@@ -34,25 +36,29 @@ struct FwdArgs {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-constexpr int kFwdBM = 128;  // query rows per workgroup
-constexpr int kFwdBN = 64;   // keys per tile
+constexpr int kFwdWaves = 8;
+constexpr int kFwdBM = 32 * kFwdWaves;  // query rows per workgroup
+template <typename T> constexpr int fwd_bn() { return sizeof(T) == 2 ? 64 : 32; }  // keys per tile
+constexpr float kRescaleSlack = 8.f;    // log2 units a stale running max may lag the true one
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   typedef Mma<T> M;
-  typedef TileDims<T, D> TD;
-  constexpr int KS = M::KS, KL = M::KL, BN = kFwdBN;
-  __shared__ __attribute__((aligned(16))) T Ks[BN * TD::RM];
-  __shared__ __attribute__((aligned(16))) T Vt[(BN / 32) * D * TD::TR];
-  __shared__ int64_t koff[BN];
+  constexpr int BN = fwd_bn<T>();
+  typedef Tile<T, D, BN> TL;
+  constexpr int KS = M::KS, KL = M::KL, NT = kFwdWaves * 64;
+  __shared__ __attribute__((aligned(16))) T lds_k[2 * TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v[2 * TL::ELEMS];
 
   const Geo& g = a.g;
-  const T* __restrict__ q = (const T*)a.q;
-  const int h = blockIdx.y;
+  const int rows_total = g.c * g.G;
+  const int nrb = (rows_total + kFwdBM - 1) / kFwdBM;
+  const int item = xcd_remap(blockIdx.x, nrb * g.hkv);
+  const int h = item / nrb;
+  const int r0 = (nrb - 1 - item % nrb) * kFwdBM;  // later (heavier) row blocks first
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
-  const int rows_total = g.c * g.G;
-  const int r0 = blockIdx.x * kFwdBM;
   const int my_row = r0 + wave * 32 + col;
   const bool row_ok = my_row < rows_total;
   const int my_t = row_ok ? my_row / g.G : g.c - 1;
@@ -60,82 +66,93 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // Q^T as B operands: lane (row col, half hh) holds Q[row][s*KS + hh*KL + i]
   typename M::frag qf[D / KS];
-  const T* qrow = q + ((int64_t)my_t * g.hq + my_g) * D;
+  const T* qrow = (const T*)a.q + ((int64_t)my_t * g.hq + my_g) * D;
 #pragma unroll
   for (int s = 0; s < D / KS; ++s) qf[s] = row_ok ? M::load(qrow + s * KS + hh * KL) : M::zero();
 
   const int pk = g.keff << g.ps_log2;
   const int last_row = min(r0 + kFwdBM, rows_total) - 1;
+  const int t_lo = r0 / g.G;
   const int nkeys = pk + last_row / g.G + 1;  // prior keys + chunk tokens up to the block's last
+  const int ntiles = (nkeys + BN - 1) / BN;
 
-  float m = -INFINITY, l = 0.f;
+  const T* __restrict__ kp = (const T*)a.k;
+  const T* __restrict__ vp = (const T*)a.v;
+  PairStages<T, D, BN, NT> kv{lds_k, lds_v};
+  // rows past the key list are clamped to its last key (finite data, masked below)
+  auto rows_from = [&](int j0) {
+    return [&, j0](int r) -> int64_t { return key_offset<D>(g, a.pt, a.sel, h, min(j0 + r, nkeys - 1)); };
+  };
+
+  float m_ref = -INFINITY, l = 0.f;  // running max (log2 domain) and this lane's partial sum
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
 
-  for (int j0 = 0; j0 < nkeys; j0 += BN) {
-    __syncthreads();
-    if (tid < BN) koff[tid] = (j0 + tid < nkeys) ? key_offset<D>(g, a.pt, a.sel, h, j0 + tid) : (int64_t)-1;
-    __syncthreads();
-    stage_tile<T, D, BN, true, false>((const T*)a.k, koff, Ks, nullptr, tid);
-    stage_tile<T, D, BN, false, true>((const T*)a.v, koff, nullptr, Vt, tid);
-    __syncthreads();
+  kv.load(0, kp, vp, tid, rows_from(0));
+  kv.commit(0, tid);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = it * BN;
+    if (it + 1 < ntiles) kv.load((it + 1) & 1, kp, vp, tid, rows_from(j0 + BN));
+    const TL tk = kv.ta(it & 1), tv = kv.tb(it & 1);
 
     f32x16 sacc[BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       sacc[kb] = zero16();
 #pragma unroll
-      for (int s = 0; s < D / KS; ++s)
-        sacc[kb] = M::mma(M::load(&Ks[(kb * 32 + col) * TD::RM + s * KS + hh * KL]), qf[s], sacc[kb]);
+      for (int s = 0; s < D / KS; ++s) sacc[kb] = M::mma(tk.frag_rm(kb * 32 + col, s, hh), qf[s], sacc[kb]);
     }
-    const bool need_mask = j0 + BN > pk;  // the tile reaches chunk tokens or the tail
+    // keys beyond the causal diagonal of some row, or past the key list
+    if (j0 + BN - 1 - pk > t_lo || j0 + BN > nkeys) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + kb * 32 + acc_row(e, hh);
+          if (j >= nkeys || (j >= pk && j - pk > my_t)) sacc[kb][e] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = sacc[kb][e] * a.scale_log2;
-        if (need_mask) {
-          const int j = j0 + kb * 32 + acc_row(e, hh);
-          if (j >= nkeys || (j >= pk && j - pk > my_t)) x = -INFINITY;
-        }
-        sacc[kb][e] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m, mx);
-    const bool any = m_new != -INFINITY;
-    const float alpha = any ? exp2f(m - m_new) : 1.f;
-    float rs = 0.f;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = wave_xor_max(mx, 32) * a.scale_log2;
+    const bool upd = mx > m_ref + kRescaleSlack;
+    if (__ballot(upd)) {
+      const float m_new = upd ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_ref = m_new;
+    }
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = any ? exp2f(sacc[kb][e] - m_new) : 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], a.scale_log2, -m_ref));
         sacc[kb][e] = p;
-        rs += p;
+        l += p;
       }
-    rs = wave_xor_sum(rs, 32);
-    l = l * alpha + rs;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
       for (int s = 0; s < 32 / KS; ++s) {
         const typename M::frag pf = M::pack(sacc[kb], s * KL);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          oacc[db] = M::mma(M::load(&Vt[kb * D * TD::TR + (db * 32 + col) * TD::TR + hh * 16 + s * KL]), pf,
-                            oacc[db]);
+        for (int db = 0; db < D / 32; ++db) oacc[db] = M::mma(tv.frag_tr(kb, db, s, lane), pf, oacc[db]);
       }
+
+    if (it + 1 < ntiles) kv.commit((it + 1) & 1, tid);
+    __syncthreads();
   }
 
+  l = wave_xor_sum(l, 32);
   if (row_ok) {
     const float inv = 1.f / l;
     T* orow = (T*)a.o + ((int64_t)my_t * g.hq + my_g) * D;
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           *reinterpret_cast<f32x4*>(orow + d) = w;
         }
       }
-    if (hh == 0) a.lse[(int64_t)my_g * g.c + my_t] = (m + log2f(l)) * kLn2;
+    if (hh == 0) a.lse[(int64_t)my_g * g.c + my_t] = (m_ref + log2f(l)) * kLn2;
   }
 }
 
@@ -173,14 +190,15 @@ hipError_t launch_fwd(const Shape& s, const void* q, const void* k_pool, const v
   a.g = make_geo(s);
   a.scale_log2 = s.scale * kLog2e;
   const int rows = s.c * (s.hq / s.hkv);
-  dim3 grid((rows + kFwdBM - 1) / kFwdBM, s.hkv);
+  const dim3 grid(((rows + kFwdBM - 1) / kFwdBM) * s.hkv);
+  const dim3 block(kFwdWaves * 64);
   Traced tr(st, "fwd_kernel");
   if (s.bf16) {
-    if (s.d == 128) hipLaunchKernelGGL((fwd_kernel<__bf16, 128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<__bf16, 64>), grid, dim3(256), 0, st, a);
+    if (s.d == 128) hipLaunchKernelGGL((fwd_kernel<__bf16, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<__bf16, 64>), grid, block, 0, st, a);
   } else {
-    if (s.d == 128) hipLaunchKernelGGL((fwd_kernel<float, 128>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((fwd_kernel<float, 64>), grid, dim3(256), 0, st, a);
+    if (s.d == 128) hipLaunchKernelGGL((fwd_kernel<float, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((fwd_kernel<float, 64>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -113,6 +113,15 @@ __device__ __forceinline__ int64_t key_offset(const Geo& g, const int32_t* __res
   return ((slot * g.hkv + h) * (int64_t)(1 << g.ps_log2) + row) * D;
 }
 
+// Workgroup b runs on XCD b % 8 (dispatch is round-robin over the 8 XCDs).
+// Map it to a work item so that each XCD gets a contiguous range of items,
+// whose K/V (or Q/dO) tiles then stay in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int per = total / 8;
+  if (b >= per * 8) return b;
+  return (b % 8) * per + b / 8;
+}
+
 // Warp-wide helpers (wave64).
 __device__ __forceinline__ float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) { return v + __shfl_xor(v, mask, 64); }

@@ -40,7 +40,10 @@ struct SelectPlan {
 SelectPlan select_plan(const Shape& s);
 
 struct BwdPlan {
-  size_t off_dt, bytes;  // Dt = rowsum(dO * O) per (head, token), fp32 [Hq][C]
+  size_t off_dt;                  // Dt = rowsum(dO * O) per (head, token), fp32 [Hq][C]
+  size_t off_part_k, off_part_v;  // dK / dV partial sums of a row split, fp32 [splits][Hkv][nkeys][D]
+  int splits;                     // workgroups sharing one key block's query rows
+  size_t bytes;
 };
 BwdPlan bwd_plan(const Shape& s);
 

@@ -1,43 +1,191 @@
-// tiles.h -- global -> LDS staging of attention tiles for the gfx950 kernels.
+// tiles.h -- LDS tiles and MFMA operand reads for the gfx950 attention kernels.
+//
+// A tile holds BR rows of D elements, row-major.  Operands read from it:
+//   frag_rm(row, s, hh): the A operand whose row is a tile row and whose
+//     contraction runs along D -- lane (row, half hh) takes elements
+//     [s*KS + hh*KL, +KL) of that row (one 16-byte read for bf16).
+//   frag_tr(rb, cb, s, lane): the A operand of the transposed tile -- its rows
+//     are the D columns cb*32 .. cb*32+31 and its contraction runs over the
+//     tile rows of the 32-row block rb, in the order in which a 32x32
+//     accumulator holds its rows (lane half hh holds rows 8*(e/4) + 4*hh + e%4,
+//     e < 16), so that an accumulator computed with tile rows as its M
+//     dimension can be fed back as the B operand of a product that contracts
+//     over those rows.
+//
+// bf16 rows are padded to 288 bytes (D = 128) or 144 bytes (D = 64) and, for
+// D = 128, rows 8..15 of every 16 swap neighbouring 16-byte chunks: then the 16
+// rows of a 16-lane group of 16-byte reads, and the 4 rows x 32 bytes of a
+// 16-lane group of transposing reads, fall in distinct LDS banks, while every
+// operand address stays affine (immediate offsets, few registers).  A bf16 tile
+// is filled straight from global memory with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a wave writes bytes [16 l, 16 l + 16) of
+// a 1 KB block; padding slots get a dummy chunk), so staging needs no
+// registers; the transposed operand is read with the gfx950 transposing LDS
+// read (ds_read_b64_tr_b16: within 16 lanes, lane i gets value i%4 of the
+// 8-byte chunk addressed by lane 4k + i/4, for k = 0..3).
+// fp32 tiles are padded, filled through registers, and keep a second,
+// transposed copy for frag_tr.
 #pragma once
 
 #include "common.h"
 
 namespace oomb {
 
-// LDS strides, in elements.  Row-major tiles pad each D-row by 16 bytes and
-// transposed tiles pad each 32-entry row by 16 bytes, so that the 16-byte
-// operand reads of consecutive lanes fall in different banks.
-template <typename T, int D> struct TileDims {
-  static constexpr int VEC = 16 / (int)sizeof(T);  // elements per 16-byte load
-  static constexpr int CPR = D / VEC;             // 16-byte loads per row
-  static constexpr int RM = D + VEC;              // row-major row stride
-  static constexpr int TR = 32 + VEC;             // transposed row stride
-};
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
 
-// Stage BR rows of D elements into LDS.  Row i starts at element off[i] of src
-// (off[i] < 0: a row of zeros).  With RMAJ the tile is written row-major,
-// rm[i * RM + d]; with TRAN it is also written transposed in operand order,
-// tr[(i / 32) * D * TR + d * TR + operand_pos(i % 32)], which is how an A
-// operand meets an accumulator reused as the B operand.
-template <typename T, int D, int BR, bool RMAJ, bool TRAN, int NT = 256>
-__device__ __forceinline__ void stage_tile(const T* __restrict__ src, const int64_t* off, T* rm, T* tr,
-                                           int tid) {
-  typedef TileDims<T, D> TD;
-#pragma unroll 2
-  for (int i = tid; i < BR * TD::CPR; i += NT) {
-    const int row = i / TD::CPR, cg = i % TD::CPR;
-    const int64_t o = off[row];
-    f32x4 raw = {0.f, 0.f, 0.f, 0.f};
-    if (o >= 0) raw = *reinterpret_cast<const f32x4*>(src + o + cg * TD::VEC);
-    if constexpr (RMAJ) *reinterpret_cast<f32x4*>(rm + row * TD::RM + cg * TD::VEC) = raw;
-    if constexpr (TRAN) {
-      const T* v = reinterpret_cast<const T*>(&raw);
-      T* dst = tr + (row >> 5) * D * TD::TR + (cg * TD::VEC) * TD::TR + operand_pos(row & 31);
-#pragma unroll
-      for (int e = 0; e < TD::VEC; ++e) dst[e * TD::TR] = v[e];
+template <typename T, int D, int BR> struct Tile;
+
+template <int D, int BR> struct Tile<__bf16, D, BR> {
+  typedef __bf16 T;
+  static constexpr int VEC = 8;                      // elements per 16-byte chunk
+  static constexpr int CPR = D / VEC;                // data chunks per row (16 or 8)
+  static constexpr int SLOTS = D == 128 ? 18 : 9;    // chunk slots per row, padding included
+  static constexpr int RS = SLOTS * VEC;             // row stride (elements): 288 B or 144 B
+  static constexpr int ELEMS = BR * RS;              // LDS elements per tile
+  static constexpr int BLOCKS = BR * SLOTS / 64;     // 1 KB blocks (one direct load per wave each)
+  static_assert(D == 128 || D == 64, "bf16 tiles support D = 64 and 128");
+  static_assert((BR * SLOTS) % 64 == 0, "tile must be whole 1 KB blocks");
+  T* rm;
+
+  // chunk position of logical chunk c in row r: for D = 128 rows 8..15 of each
+  // 16 swap neighbouring chunks, which puts the 16 rows of a 16-byte read in 16
+  // distinct bank groups; the addresses stay affine in the chunk index
+  __device__ static __forceinline__ int flip(int r) { return D == 128 ? (r >> 3) & 1 : 0; }
+
+  // Direct global -> LDS fill of this tile by `nwaves` waves.  off(r): element
+  // offset in src of tile row r (callers clamp rows past the end to a real one).
+  // Padding slots are filled from the row's first chunk.
+  template <typename OffFn>
+  __device__ __forceinline__ void fill(const T* __restrict__ src, int wave, int nwaves, int lane, OffFn off) const {
+    for (int b = wave; b < BLOCKS; b += nwaves) {
+      const int q = b * 64 + lane;
+      const int r = q / SLOTS, p = q % SLOTS;
+      const int c = p < CPR ? (p ^ flip(r)) : 0;
+      __builtin_amdgcn_global_load_lds((gbl_void*)(src + off(r) + c * VEC), (lds_void*)(rm + b * 512), 16, 0, 0);
     }
   }
-}
+  __device__ __forceinline__ bf16x8 frag_rm(int row, int s, int hh) const {
+    return *reinterpret_cast<const bf16x8*>(rm + row * RS + ((2 * s + hh) ^ flip(row)) * VEC);
+  }
+  __device__ __forceinline__ bf16x8 frag_tr(int rb, int cb, int s, int lane) const {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = rb * 32 + 16 * s + 4 * (g >> 1) + (j >> 2);
+    const int c = 4 * cb + 2 * (g & 1) + ((j & 3) >> 1);
+    const int half = (j & 1) * 4;
+    const T* p0 = rm + row * RS + (c ^ flip(row)) * VEC + half;
+    const T* p1 = rm + (row + 8) * RS + (c ^ flip(row + 8)) * VEC + half;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
+    bf16x8 f;
+    const __bf16* pa = reinterpret_cast<const __bf16*>(&a);
+    const __bf16* pb = reinterpret_cast<const __bf16*>(&b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[i] = pa[i];
+      f[4 + i] = pb[i];
+    }
+    return f;
+  }
+};
+
+// fp32: row-major copy (stride D+4) plus a transposed copy in operand order,
+// tr[(row/32) * D * TRS + d * TRS + operand_pos(row % 32)], TRS = 36.
+template <int D, int BR> struct Tile<float, D, BR> {
+  typedef float T;
+  static constexpr int VEC = 4;
+  static constexpr int CPR = D / VEC;
+  static constexpr int RS = D + 4;
+  static constexpr int TRS = 36;
+  static constexpr int ELEMS = BR * RS + (BR / 32) * D * TRS;
+  T* rm;
+
+  __device__ __forceinline__ void put(int row, int cg, const f32x4& v) const {
+    *reinterpret_cast<f32x4*>(rm + row * RS + cg * VEC) = v;
+    T* tr = rm + BR * RS + (row >> 5) * D * TRS + (cg * VEC) * TRS + operand_pos(row & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tr[e * TRS] = v[e];
+  }
+  __device__ __forceinline__ float frag_rm(int row, int s, int hh) const { return rm[row * RS + s * 2 + hh]; }
+  __device__ __forceinline__ float frag_tr(int rb, int cb, int s, int lane) const {
+    const int col = lane & 31, hh = lane >> 5;
+    return rm[BR * RS + rb * D * TRS + (cb * 32 + col) * TRS + hh * 16 + s];
+  }
+};
+
+// Register staging for fp32 tiles: NT threads each carry N 16-byte chunks;
+// chunk c of the tile is (row c / CPR, column group c % CPR).
+template <int D, int BR, int NT> struct Stager {
+  typedef Tile<float, D, BR> TL;
+  static constexpr int N = (BR * TL::CPR + NT - 1) / NT;
+  f32x4 v[N];
+
+  template <typename OffFn>
+  __device__ __forceinline__ void load(const float* __restrict__ src, int tid, OffFn off) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT;
+      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < BR * TL::CPR) v[i] = *reinterpret_cast<const f32x4*>(src + off(c / TL::CPR) + (c % TL::CPR) * 4);
+    }
+  }
+  __device__ __forceinline__ void store(const TL& t, int tid) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int c = tid + i * NT;
+      if (c < BR * TL::CPR) t.put(c / TL::CPR, c % TL::CPR, v[i]);
+    }
+  }
+};
+
+// Waits until this wave's direct-to-LDS loads have landed.
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Two tensors with the same row addressing (K and V, or Q and dO), staged in
+// double-buffered tiles.  load(stage, ...) starts the copy of the next tiles;
+// commit(stage) finishes it for this thread (bf16: wait for the direct loads;
+// fp32: write the staged registers).  A barrier must follow commit before any
+// wave reads the stage.
+template <typename T, int D, int BR, int NT> struct PairStages {
+  typedef Tile<T, D, BR> TL;
+  static constexpr bool kDirect = sizeof(T) == 2;
+  T* pa;  // stage s of tensor a: pa + s * TL::ELEMS
+  T* pb;
+  Stager<D, BR, NT> sa, sb;
+
+  __device__ __forceinline__ TL ta(int s) const { return TL{pa + s * TL::ELEMS}; }
+  __device__ __forceinline__ TL tb(int s) const { return TL{pb + s * TL::ELEMS}; }
+
+  template <typename OffFn>
+  __device__ __forceinline__ void load(int stage, const T* __restrict__ srca, const T* __restrict__ srcb, int tid,
+                                       OffFn off) {
+    if constexpr (kDirect) {
+      const int wave = tid >> 6, lane = tid & 63;
+      T* da = pa + stage * TL::ELEMS;
+      T* db = pb + stage * TL::ELEMS;
+      for (int blk = wave; blk < TL::BLOCKS; blk += NT / 64) {
+        const int q = blk * 64 + lane;
+        const int r = q / TL::SLOTS, p = q % TL::SLOTS;
+        const int c = p < TL::CPR ? (p ^ TL::flip(r)) : 0;
+        const int64_t o = off(r) + c * TL::VEC;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(srca + o), (lds_void*)(da + blk * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(srcb + o), (lds_void*)(db + blk * 512), 16, 0, 0);
+      }
+    } else {
+      sa.load((const float*)srca, tid, off);
+      sb.load((const float*)srcb, tid, off);
+    }
+  }
+  __device__ __forceinline__ void commit(int stage, int tid) {
+    if constexpr (kDirect) {
+      wait_lds_loads();
+    } else {
+      sa.store(Tile<float, D, BR>{(float*)pa + stage * TL::ELEMS}, tid);
+      sb.store(Tile<float, D, BR>{(float*)pb + stage * TL::ELEMS}, tid);
+    }
+  }
+};
 
 }  // namespace oomb
