@@ -88,7 +88,8 @@ typedef struct {
   int32_t n_kv_heads;     /* Hkv > 0, Hq % Hkv == 0, Hkv * D <= 1024 */
   int32_t head_dim;       /* D in {64, 128} */
   int32_t page_size;      /* ps in {16, 32, 64, 128} */
-  int32_t chunk_len;      /* C > 0, C % ps == 0, C * Hq < 2^30 */
+  int32_t chunk_len;      /* C > 0, C % ps == 0, C * Hq < 2^30,
+                             C * Hq / Hkv < 2^24, Hq / Hkv < 1024 */
   int32_t n_prior_pages;  /* N >= 0: candidate logical pages 0 .. N-1 */
   int32_t top_k;          /* >= 0; K_eff = min(top_k, N); top_k >= N attends every prior page;
                              K_eff * ps + C < 2^30 */

@@ -43,9 +43,10 @@ int validate(const oomb_desc* d, oomb::Shape* s) {
   if (ps_log2 < 4 || ps_log2 > 7) return OOMB_ERR_UNSUPPORTED;
   if ((int64_t)d->n_kv_heads * d->head_dim > 1024) return OOMB_ERR_UNSUPPORTED;
   const int64_t G = d->n_q_heads / d->n_kv_heads;
+  if (G >= 1024) return OOMB_ERR_UNSUPPORTED;
   const int64_t keff = d->top_k < d->n_prior_pages ? d->top_k : d->n_prior_pages;
   // 32-bit row and key indices inside the kernels
-  if ((int64_t)d->chunk_len * G >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
+  if ((int64_t)d->chunk_len * G >= (1ll << 24)) return OOMB_ERR_UNSUPPORTED;
   if (keff * d->page_size + d->chunk_len >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
   if ((int64_t)d->chunk_len * d->n_q_heads >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
   s->hq = d->n_q_heads;

@@ -8,8 +8,8 @@
 //
 // Kernels, in stream order:
 //   1. dt_kernel:   Dt[g][t] = dO[t][g] . O[t][g]                 (HBM-bound)
-//   2. dkdv_kernel: key-major.  A workgroup owns 256 keys of one kv-head's key
-//      list (4 waves x 64 keys; K and V stay in registers) and walks a share of
+//   2. dkdv_kernel: key-major.  A workgroup owns 128 keys of one kv-head's key
+//      list (4 waves x 32 keys; V in registers, K in LDS) and walks a share of
 //      the query rows that see them in tiles of 64 rows, recomputing
 //      S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
 //      dK^T += Q^T dS (dO^T and Q^T read transposed from the row-major LDS
@@ -42,7 +42,8 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* dt;       // workspace [Hq][C]
+  float* dt;       // workspace [Hq][C]: rowsum(dO * O)
+  float* lse2;     // workspace [Hq][C]: lse * log2(e)
   float* part_k;   // workspace [splits][Hkv][nkeys][D], scaled dK partials
   float* part_v;   // workspace [splits][Hkv][nkeys][D]
   int splits;
@@ -51,7 +52,7 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Dt = rowsum(dO * O), one row per group of D/VEC lanes.
+// Dt = rowsum(dO * O) and lse in log2 units, one row per group of D/VEC lanes.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dt_kernel(BwdArgs a) {
@@ -74,19 +75,22 @@ __global__ __launch_bounds__(256) void dt_kernel(BwdArgs a) {
   for (int m = LPR / 2; m >= 1; m >>= 1) s = wave_xor_sum(s, m);
   if (row < rows && lane_in_row == 0) {
     const int t = row / a.g.hq, g = row % a.g.hq;  // row = t * Hq + g
-    a.dt[(int64_t)g * a.g.c + t] = s;
+    const int64_t i = (int64_t)g * a.g.c + t;
+    a.dt[i] = s;
+    a.lse2[i] = a.lse[i] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV, key-major.  Four waves (one per SIMD, so up to 512 registers each);
-// a wave owns NKB key blocks of 32 keys (64 keys for bf16): every A operand
-// read from LDS then feeds NKB MFMAs.
+// dK / dV, key-major.  Four waves own 32 keys each: V^T fragments stay in
+// registers and the dK^T / dV^T accumulators too.  bf16: the workgroup's K rows
+// are staged once in LDS as the B operand of S = Q K^T, which keeps a wave
+// within 256 registers, so two workgroups share a CU and one wave's softmax
+// overlaps the other's MFMAs.  fp32: K fragments in registers.
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
-template <typename T> constexpr int kv_nkb() { return sizeof(T) == 2 ? 2 : 1; }  // 32-key blocks per wave
-template <typename T> constexpr int kv_keys() { return kKvWaves * 32 * kv_nkb<T>(); }  // keys per workgroup
-template <typename T> constexpr int kv_bm() { return sizeof(T) == 2 ? 64 : 32; }  // query rows per tile
+template <typename T> constexpr int kv_waves() { return 4; }
+template <typename T> constexpr int kv_keys() { return kv_waves<T>() * 32; }  // keys per workgroup
+template <typename T, int D> constexpr int kv_bm() { return sizeof(T) == 2 && D == 64 ? 64 : 32; }  // rows per tile
 
 struct KvPlan {
   int nkb, splits;
@@ -97,21 +101,49 @@ __host__ __device__ inline KvPlan kv_plan(const Geo& g, int keys_per_wg) {
   const int nkeys = (g.keff << g.ps_log2) + g.c;
   p.nkb = (nkeys + keys_per_wg - 1) / keys_per_wg;
   const int items = p.nkb * g.hkv;
-  int s = (512 + items - 1) / items;  // at least two workgroups per CU over the launch
+  int s = (1536 + items - 1) / items;  // about three rounds of two workgroups per CU
   p.splits = s < 1 ? 1 : (s > 8 ? 8 : s);
   return p;
 }
 
+template <typename T, int D> struct KeyStore;  // where a wave's K^T B operands live
+
+template <int D> struct KeyStore<__bf16, D> {  // LDS, one tile for the workgroup
+  typedef Tile<__bf16, D, kv_keys<__bf16>()> TK;
+  TK t;
+  int row0;  // this wave's first key row in the tile
+  template <typename OffFn>
+  __device__ __forceinline__ void load(const __bf16* src, int wave, int lane, int tid, OffFn off) {
+    row0 = wave * 32;
+    t.fill(src, wave, kv_waves<__bf16>(), lane, off);
+  }
+  __device__ __forceinline__ bf16x8 frag(int s, int col, int hh) const { return t.frag_rm(row0 + col, s, hh); }
+};
+
+template <int D> struct KeyStore<float, D> {  // registers
+  float f[D / 2];
+  template <typename OffFn>
+  __device__ __forceinline__ void load(const float* src, int wave, int lane, int tid, OffFn off) {
+    const int64_t o = off(wave * 32 + (lane & 31));
+#pragma unroll
+    for (int s = 0; s < D / 2; ++s) f[s] = src[o + 2 * s + (lane >> 5)];
+  }
+  __device__ __forceinline__ float frag(int s, int col, int hh) const { return f[s]; }
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kv_waves<T>() * 64, sizeof(T) == 2 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
   typedef Mma<T> M;
-  constexpr int BM = kv_bm<T>(), NKB = kv_nkb<T>(), KEYS = kv_keys<T>();
+  constexpr int BM = kv_bm<T, D>(), KEYS = kv_keys<T>(), NW = kv_waves<T>(), NT = NW * 64;
   typedef Tile<T, D, BM> TL;
-  constexpr int KS = M::KS, KL = M::KL, NT = kKvWaves * 64;
-  __shared__ __attribute__((aligned(16))) T lds_q[2 * TL::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_d[2 * TL::ELEMS];
-  __shared__ float rlse[2][BM], rdt[2][BM];
-  __shared__ int rtok[2][BM];
+  constexpr int KS = M::KS, KL = M::KL;
+  constexpr bool kKeysInLds = sizeof(T) == 2;
+  typedef Ring<T, D, BM, NT> QD;
+  __shared__ __attribute__((aligned(16))) T lds_q[QD::NS * TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_d[QD::NS * TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_keys[kKeysInLds ? KeyStore<__bf16, D>::TK::ELEMS : 1];
+  __shared__ __attribute__((aligned(16))) float rlse[QD::NS][BM];  // per tile row: lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float rdt[QD::NS][BM];   // per tile row: Dt
 
   const Geo& g = a.g;
   const KvPlan plan = kv_plan(g, KEYS);
@@ -126,182 +158,158 @@ __global__ __launch_bounds__(kKvWaves * 64) void dkdv_kernel(BwdArgs a) {
   const int nkeys = pk + g.c;
   const int jb = kblk * KEYS;
 
-  // this lane's keys (one per 32-key block) and their K^T / V^T B operands:
-  // lane (key col, half hh) holds K[key][s*KS + hh*KL + i]
-  int my_key[NKB], my_u[NKB];
-  bool key_ok[NKB];
-  int64_t koff[NKB];
-  typename M::frag kf[NKB][D / KS], vf[NKB][D / KS];
+  // this lane's key and its V^T B operands: lane (key col, half hh) holds
+  // V[key][s*KS + hh*KL + i]
+  const int my_key = jb + wave * 32 + col;
+  const bool key_ok = my_key < nkeys;
+  const int64_t koff = key_ok ? key_offset<D>(g, a.pt, a.sel, h, my_key) : 0;
+  const int my_u = my_key - pk;  // chunk token index when >= 0
+  typename M::frag vf[D / KS];
 #pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    my_key[kk] = jb + (wave * NKB + kk) * 32 + col;
-    key_ok[kk] = my_key[kk] < nkeys;
-    koff[kk] = key_ok[kk] ? key_offset<D>(g, a.pt, a.sel, h, my_key[kk]) : 0;
-    my_u[kk] = my_key[kk] - pk;  // chunk token index when >= 0
-#pragma unroll
-    for (int s = 0; s < D / KS; ++s) {
-      kf[kk][s] = key_ok[kk] ? M::load((const T*)a.k + koff[kk] + s * KS + hh * KL) : M::zero();
-      vf[kk][s] = key_ok[kk] ? M::load((const T*)a.v + koff[kk] + s * KS + hh * KL) : M::zero();
-    }
-  }
-  f32x16 dkacc[NKB][D / 32], dvacc[NKB][D / 32];
-#pragma unroll
-  for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      dkacc[kk][db] = zero16();
-      dvacc[kk][db] = zero16();
-    }
+  for (int s = 0; s < D / KS; ++s) vf[s] = key_ok ? M::load((const T*)a.v + koff + s * KS + hh * KL) : M::zero();
+  KeyStore<T, D> ks;
+  if constexpr (kKeysInLds) ks.t.rm = lds_keys;
+  // keys past the list are clamped to its last key (finite data, zero weight below)
+  ks.load((const T*)a.k, wave, lane, tid,
+          [&](int r) -> int64_t { return key_offset<D>(g, a.pt, a.sel, h, min(jb + r, nkeys - 1)); });
+  if constexpr (kKeysInLds) wait_vmem_le(0);
 
-  // rows that can see a key of this block: all rows for prior keys, else rows
-  // of chunk tokens t >= the block's first chunk token; this split's share
-  const int rows_total = g.c * g.G;
-  const int row_start = jb < pk ? 0 : (jb - pk) * g.G;
-  const int ntile_all = (rows_total - row_start + BM - 1) / BM;
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dkacc[db] = zero16();
+    dvacc[db] = zero16();
+  }
+
+  // Query rows are visited head by head: tile (gi, t0) holds tokens t0 .. t0+BM-1
+  // of query head h*G + gi, which sit hq*D elements apart in Q and dO.  Rows
+  // that can see a key of this block: every token for prior keys, else tokens
+  // t >= the block's first chunk token (t0 starts at that token rounded down
+  // to a tile).  Tokens past the chunk read the last token (finite data, zero
+  // weight below).  This split takes a contiguous share of the tiles.
+  const int t_first = jb < pk ? 0 : ((jb - pk) / BM) * BM;
+  const int tiles_per_head = (g.c - t_first + BM - 1) / BM;
+  const int ntile_all = tiles_per_head * g.G;
   const int tile_lo = (int)((int64_t)ntile_all * sp / plan.splits);
   const int tile_hi = (int)((int64_t)ntile_all * (sp + 1) / plan.splits);
+  const int ntiles = tile_hi - tile_lo;
+  auto tile_head = [&](int j) { return (tile_lo + j) / tiles_per_head; };
+  auto tile_t0 = [&](int j) { return t_first + ((tile_lo + j) % tiles_per_head) * BM; };
 
   const T* __restrict__ qp = (const T*)a.q;
   const T* __restrict__ dp = (const T*)a.dout;
-  PairStages<T, D, BM, NT> qd{lds_q, lds_d};
-  // rows past the end are clamped to the last row (finite data, zero weight below)
-  auto rows_from = [&](int r0) {
-    return [&, r0](int r) -> int64_t {
-      const int rr = min(r0 + r, rows_total - 1);
-      return ((int64_t)(rr / g.G) * g.hq + h * g.G + rr % g.G) * D;
-    };
-  };
-  float nlse = 0.f, ndt = 0.f;
-  int ntok = -1;
-  auto fetch = [&](int r0, int stage) {
-    qd.load(stage, qp, dp, tid, rows_from(r0));
-    if (tid < BM) {
-      const int r = r0 + tid;
-      ntok = -1;
-      nlse = 0.f;
-      ndt = 0.f;
-      if (r < rows_total) {
-        const int t = r / g.G, qh = h * g.G + r % g.G;
-        ntok = t;
-        nlse = a.lse[(int64_t)qh * g.c + t] * kLog2e;
-        ndt = a.dt[(int64_t)qh * g.c + t];
-      }
+  QD qd{lds_q, lds_d};
+  const int64_t tok_stride = (int64_t)g.hq * D;
+  auto load = [&](int j) {
+    const int gi = tile_head(j), t0 = tile_t0(j);
+    const int tmax = g.c - 1 - t0;  // last valid row of the tile
+    const int64_t base = ((int64_t)t0 * g.hq + h * g.G + gi) * D;
+    qd.load(j, qp, dp, tid, [=](int r) -> int64_t { return base + (int64_t)min(r, tmax) * tok_stride; });
+    if (wave == 0 && lane < BM) {
+      const int64_t i = (int64_t)(h * g.G + gi) * g.c + t0 + min(lane, tmax);
+      load_lds_dword(a.lse2 + i, rlse[j % QD::NS]);
+      load_lds_dword(a.dt + i, rdt[j % QD::NS]);
     }
   };
-  auto stash = [&](int stage) {
-    qd.commit(stage, tid);
-    if (tid < BM) {
-      rlse[stage][tid] = nlse;
-      rdt[stage][tid] = ndt;
-      rtok[stage][tid] = ntok;
-    }
-  };
+  const int vm_per_tile = QD::loads_per_tile(wave) + (wave == 0 ? 2 : 0);
 
-  if (tile_lo < tile_hi) {
-    fetch(row_start + tile_lo * BM, 0);
-    stash(0);
-  }
-  __syncthreads();
-  for (int it = tile_lo; it < tile_hi; ++it) {
-    const int stage = (it - tile_lo) & 1;
-    if (it + 1 < tile_hi) fetch(row_start + (it + 1) * BM, stage ^ 1);
-    const TL tq = qd.ta(stage), td = qd.tb(stage);
+  // a 32-row block needs no per-element visibility test when every row is a
+  // real token and every key of this wave is a valid prior key or a chunk
+  // token no later than the block's first token
+  const int wave_last = jb + wave * 32 + 31;  // last key of this wave
+  const bool wave_keys_ok = wave_last < nkeys;
+  const bool wave_prior = wave_last < pk;
+
+  for (int j = 0; j < QD::PD && j < ntiles; ++j) load(j);
+  for (int it = 0; it < ntiles; ++it) {
+    qd.commit(it, min(QD::PD - 1, ntiles - 1 - it), vm_per_tile, tid);
+    if constexpr (!QD::kDirect) {
+      if (wave == 0) wait_vmem_le(0);  // the row metadata loads
+    }
+    __syncthreads();
+    if (it + QD::PD < ntiles) load(it + QD::PD);
+    const TL tq = qd.ta(it), td = qd.tb(it);
+    const float* ml = rlse[it % QD::NS];
+    const float* md = rdt[it % QD::NS];
+    const int t0 = tile_t0(it);
 #pragma unroll 1
     for (int rb = 0; rb < BM / 32; ++rb) {
-      f32x16 sacc[NKB], pacc[NKB];
+      f32x16 sacc = zero16(), pacc = zero16();
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) {
-        sacc[kk] = zero16();
-        pacc[kk] = zero16();
-      }
+      for (int s = 0; s < D / KS; ++s) sacc = M::mma(tq.frag_rm(rb * 32 + col, s, hh), ks.frag(s, col, hh), sacc);
 #pragma unroll
-      for (int s = 0; s < D / KS; ++s) {
-        const typename M::frag fq = tq.frag_rm(rb * 32 + col, s, hh);
+      for (int s = 0; s < D / KS; ++s) pacc = M::mma(td.frag_rm(rb * 32 + col, s, hh), vf[s], pacc);
+      // element e of a lane: query token tb + acc_row(e, hh) of head gi, key my_key
+      const int tb = t0 + rb * 32;
+      const bool full = tb + 32 <= g.c && wave_keys_ok && (wave_prior || tb >= wave_last - pk);
+      if (full) {
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) sacc[kk] = M::mma(fq, kf[kk][s], sacc[kk]);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int r = rb * 32 + acc_row(e, hh);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -ml[r]));
+          sacc[e] = p;
+          pacc[e] = p * (pacc[e] - md[r]);
+        }
+      } else {
 #pragma unroll
-      for (int s = 0; s < D / KS; ++s) {
-        const typename M::frag fd = td.frag_rm(rb * 32 + col, s, hh);
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) pacc[kk] = M::mma(fd, vf[kk][s], pacc[kk]);
-      }
-      // element e of a lane: query row rb*32 + acc_row(e, hh), key my_key[kk]
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = rb * 32 + acc_row(e, hh);
-        const int t = rtok[stage][r];
-        const float l2 = rlse[stage][r], dt = rdt[stage][r];
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) {
-          const bool vis = key_ok[kk] && t >= 0 && my_u[kk] <= t;  // my_u < 0 for prior keys
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[kk][e], a.scale_log2, -l2)) : 0.f;
-          sacc[kk][e] = p;
-          pacc[kk][e] = p * (pacc[kk][e] - dt);
+        for (int e = 0; e < 16; ++e) {
+          const int r = rb * 32 + acc_row(e, hh);
+          const int t = tb + acc_row(e, hh);
+          const bool vis = key_ok && t < g.c && my_u <= t;  // my_u < 0 for prior keys
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -ml[r])) : 0.f;
+          sacc[e] = p;
+          pacc[e] = p * (pacc[e] - md[r]);
         }
       }
 #pragma unroll
       for (int s = 0; s < 32 / KS; ++s) {
-        typename M::frag pf[NKB], sf[NKB];
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) {
-          pf[kk] = M::pack(sacc[kk], s * KL);
-          sf[kk] = M::pack(pacc[kk], s * KL);
-        }
+        const typename M::frag pf = M::pack(sacc, s * KL);
+        const typename M::frag sf = M::pack(pacc, s * KL);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const typename M::frag fdt = td.frag_tr(rb, db, s, lane);
-#pragma unroll
-          for (int kk = 0; kk < NKB; ++kk) dvacc[kk][db] = M::mma(fdt, pf[kk], dvacc[kk][db]);
-          const typename M::frag fqt = tq.frag_tr(rb, db, s, lane);
-#pragma unroll
-          for (int kk = 0; kk < NKB; ++kk) dkacc[kk][db] = M::mma(fqt, sf[kk], dkacc[kk][db]);
+          dvacc[db] = M::mma(td.frag_tr(rb, db, s, lane), pf, dvacc[db]);
+          dkacc[db] = M::mma(tq.frag_tr(rb, db, s, lane), sf, dkacc[db]);
         }
       }
     }
-    if (it + 1 < tile_hi) stash(stage ^ 1);
-    __syncthreads();
   }
 
+  if (!key_ok) return;
   const float sc = g.scale;
+  if (plan.splits == 1) {
+    float* dkp = a.dk + koff;
+    float* dvp = a.dv + koff;
 #pragma unroll
-  for (int kk = 0; kk < NKB; ++kk) {
-    if (!key_ok[kk]) continue;
-    if (plan.splits == 1) {
-      float* dkp = a.dk + koff[kk];
-      float* dvp = a.dv + koff[kk];
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = db * 32 + 8 * e4 + 4 * hh;
+        f32x4 ok = *reinterpret_cast<f32x4*>(dkp + d);
+        f32x4 ov = *reinterpret_cast<f32x4*>(dvp + d);
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int d = db * 32 + 8 * e4 + 4 * hh;
-          f32x4 ok = *reinterpret_cast<f32x4*>(dkp + d);
-          f32x4 ov = *reinterpret_cast<f32x4*>(dvp + d);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ok[i] += sc * dkacc[kk][db][4 * e4 + i];
-            ov[i] += dvacc[kk][db][4 * e4 + i];
-          }
-          *reinterpret_cast<f32x4*>(dkp + d) = ok;
-          *reinterpret_cast<f32x4*>(dvp + d) = ov;
+        for (int i = 0; i < 4; ++i) {
+          ok[i] += sc * dkacc[db][4 * e4 + i];
+          ov[i] += dvacc[db][4 * e4 + i];
         }
-    } else {
-      const int64_t base = (((int64_t)sp * g.hkv + h) * nkeys + my_key[kk]) * D;
+        *reinterpret_cast<f32x4*>(dkp + d) = ok;
+        *reinterpret_cast<f32x4*>(dvp + d) = ov;
+      }
+  } else {
+    const int64_t base = (((int64_t)sp * g.hkv + h) * nkeys + my_key) * D;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int d = db * 32 + 8 * e4 + 4 * hh;
-          f32x4 wk, wv;
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int d = db * 32 + 8 * e4 + 4 * hh;
+        f32x4 wk, wv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            wk[i] = sc * dkacc[kk][db][4 * e4 + i];
-            wv[i] = dvacc[kk][db][4 * e4 + i];
-          }
-          *reinterpret_cast<f32x4*>(a.part_k + base + d) = wk;
-          *reinterpret_cast<f32x4*>(a.part_v + base + d) = wv;
+        for (int i = 0; i < 4; ++i) {
+          wk[i] = sc * dkacc[db][4 * e4 + i];
+          wv[i] = dvacc[db][4 * e4 + i];
         }
-    }
+        *reinterpret_cast<f32x4*>(a.part_k + base + d) = wk;
+        *reinterpret_cast<f32x4*>(a.part_v + base + d) = wv;
+      }
   }
 }
 
@@ -342,10 +350,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
   typedef Mma<T> M;
   constexpr int BN = dq_bn<T>();
-  typedef Tile<T, D, BN> TL;
-  constexpr int KS = M::KS, KL = M::KL, NT = kDqWaves * 64;
-  __shared__ __attribute__((aligned(16))) T lds_k[2 * TL::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_v[2 * TL::ELEMS];
+  constexpr int NT = kDqWaves * 64;
+  typedef Ring<T, D, BN, NT> KV;
+  typedef typename KV::TL TL;
+  constexpr int KS = M::KS, KL = M::KL;
+  __shared__ __attribute__((aligned(16))) T lds_k[KV::NS * TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v[KV::NS * TL::ELEMS];
+  __shared__ int page_tab[kPageCache];
 
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
@@ -358,8 +369,8 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
   const int col = lane & 31, hh = lane >> 5;
   const int my_row = r0 + wave * 32 + col;
   const bool row_ok = my_row < rows_total;
-  const int my_t = row_ok ? my_row / g.G : g.c - 1;
-  const int my_g = h * g.G + (row_ok ? my_row % g.G : 0);
+  const int my_t = row_ok ? div_g(g, my_row) : g.c - 1;
+  const int my_g = h * g.G + (row_ok ? my_row - div_g(g, my_row) * g.G : 0);
   const int64_t qoff = ((int64_t)my_t * g.hq + my_g) * D;
 
   typename M::frag qf[D / KS], df[D / KS];
@@ -368,33 +379,46 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
     qf[s] = row_ok ? M::load((const T*)a.q + qoff + s * KS + hh * KL) : M::zero();
     df[s] = row_ok ? M::load((const T*)a.dout + qoff + s * KS + hh * KL) : M::zero();
   }
-  const float my_lse = row_ok ? a.lse[(int64_t)my_g * g.c + my_t] * kLog2e : 0.f;
+  const float my_lse = row_ok ? a.lse2[(int64_t)my_g * g.c + my_t] : 0.f;
   const float my_dt = row_ok ? a.dt[(int64_t)my_g * g.c + my_t] : 0.f;
 
   const int pk = g.keff << g.ps_log2;
   const int last_row = min(r0 + kDqBM, rows_total) - 1;
-  const int t_lo = r0 / g.G;
-  const int nkeys = pk + last_row / g.G + 1;
+  const int t_lo = div_g(g, r0);
+  const int nkeys = pk + div_g(g, last_row) + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
+  PageSlots<kPageCache> pages{page_tab};
+  pages.fill(g, a.pt, a.sel, h, (nkeys + (1 << g.ps_log2) - 1) >> g.ps_log2, tid, NT);
+  __syncthreads();
 
   const T* __restrict__ kp = (const T*)a.k;
   const T* __restrict__ vp = (const T*)a.v;
-  PairStages<T, D, BN, NT> kv{lds_k, lds_v};
-  auto rows_from = [&](int j0) {
-    return [&, j0](int r) -> int64_t { return key_offset<D>(g, a.pt, a.sel, h, min(j0 + r, nkeys - 1)); };
+  KV kv{lds_k, lds_v};
+  // one page lookup per tile when the tile lies inside a page (see the forward)
+  const bool tile_in_page = BN <= (1 << g.ps_log2);
+  auto load = [&](int j) {
+    if (tile_in_page) {
+      const int64_t base = pages.key_offset<D>(g, a.pt, a.sel, h, j * BN);
+      kv.load(j, kp, vp, tid, [base](int r) -> int64_t { return base + (int64_t)r * D; });
+    } else {
+      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t {
+        return pages.key_offset<D>(g, a.pt, a.sel, h, min(j * BN + r, nkeys - 1));
+      });
+    }
   };
+  const int vm_per_tile = KV::loads_per_tile(wave);
 
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) qacc[db] = zero16();
 
-  kv.load(0, kp, vp, tid, rows_from(0));
-  kv.commit(0, tid);
-  __syncthreads();
+  for (int j = 0; j < KV::PD && j < ntiles; ++j) load(j);
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * BN;
-    if (it + 1 < ntiles) kv.load((it + 1) & 1, kp, vp, tid, rows_from(j0 + BN));
-    const TL tk = kv.ta(it & 1), tv = kv.tb(it & 1);
+    kv.commit(it, min(KV::PD - 1, ntiles - 1 - it), vm_per_tile, tid);
+    __syncthreads();
+    if (it + KV::PD < ntiles) load(it + KV::PD);
+    const TL tk = kv.ta(it), tv = kv.tb(it);
     const bool masked = j0 + BN - 1 - pk > t_lo || j0 + BN > nkeys;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
@@ -418,8 +442,6 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
         for (int db = 0; db < D / 32; ++db) qacc[db] = M::mma(tk.frag_tr(kb, db, s, lane), sf, qacc[db]);
       }
     }
-    if (it + 1 < ntiles) kv.commit((it + 1) & 1, tid);
-    __syncthreads();
   }
 
   if (row_ok) {
@@ -443,8 +465,10 @@ BwdPlan bwd_plan(const Shape& s) {
   BwdPlan p;
   const KvPlan kp = kv_plan(make_geo(s), s.bf16 ? kv_keys<__bf16>() : kv_keys<float>());
   const size_t nkeys = (size_t)s.keff * s.ps + s.c;
+  const size_t rowvec = (((size_t)s.hq * s.c * 4) + 255) & ~(size_t)255;
   p.off_dt = 0;
-  size_t off = (((size_t)s.hq * s.c * 4) + 255) & ~(size_t)255;
+  p.off_lse2 = rowvec;
+  size_t off = 2 * rowvec;
   p.splits = kp.splits;
   p.off_part_k = off;
   const size_t part = kp.splits > 1 ? (size_t)kp.splits * s.hkv * nkeys * s.d * 4 : 0;
@@ -466,7 +490,7 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const KvPlan kp = kv_plan(a.g, kv_keys<T>());
   {
     Traced tr(st, "dkdv_kernel");
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(kp.nkb * kp.splits * a.g.hkv), dim3(kKvWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(kp.nkb * kp.splits * a.g.hkv), dim3(kv_waves<T>() * 64), 0, st, a);
   }
   if (kp.splits > 1) {
     const int64_t nkeys = (a.g.keff << a.g.ps_log2) + a.g.c;
@@ -500,6 +524,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const v
   a.dk = dk_pool;
   a.dv = dv_pool;
   a.dt = (float*)((char*)ws + p.off_dt);
+  a.lse2 = (float*)((char*)ws + p.off_lse2);
   a.part_k = (float*)((char*)ws + p.off_part_k);
   a.part_v = (float*)((char*)ws + p.off_part_v);
   a.splits = p.splits;

@@ -9,7 +9,7 @@
 // Work split: one workgroup = one kv-head h and 256 query rows of that head's
 // C*G rows (row r = token r / G, query head h*G + r % G), so every K/V tile
 // staged in LDS serves all G query heads of the group.  Eight waves own 32 rows
-// each (two waves per SIMD, so one wave's softmax overlaps another's MFMA).
+// each (two per SIMD).
 // Scores are computed transposed, S^T = K Q^T on bf16 MFMA 32x32x16 (fp32
 // MFMA 32x32x2 for fp32 inputs): a lane owns one query row, and the softmax
 // max and sum are in-lane plus one cross-half exchange.  P^T (rounded to the
@@ -44,11 +44,13 @@ constexpr float kRescaleSlack = 8.f;    // log2 units a stale running max may la
 template <typename T, int D>
 __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   typedef Mma<T> M;
-  constexpr int BN = fwd_bn<T>();
-  typedef Tile<T, D, BN> TL;
-  constexpr int KS = M::KS, KL = M::KL, NT = kFwdWaves * 64;
-  __shared__ __attribute__((aligned(16))) T lds_k[2 * TL::ELEMS];
-  __shared__ __attribute__((aligned(16))) T lds_v[2 * TL::ELEMS];
+  constexpr int BN = fwd_bn<T>(), NT = kFwdWaves * 64;
+  typedef Ring<T, D, BN, NT> KV;
+  typedef typename KV::TL TL;
+  constexpr int KS = M::KS, KL = M::KL;
+  __shared__ __attribute__((aligned(16))) T lds_k[KV::NS * TL::ELEMS];
+  __shared__ __attribute__((aligned(16))) T lds_v[KV::NS * TL::ELEMS];
+  __shared__ int page_tab[kPageCache];
 
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   const int col = lane & 31, hh = lane >> 5;
   const int my_row = r0 + wave * 32 + col;
   const bool row_ok = my_row < rows_total;
-  const int my_t = row_ok ? my_row / g.G : g.c - 1;
-  const int my_g = h * g.G + (row_ok ? my_row % g.G : 0);
+  const int my_t = row_ok ? div_g(g, my_row) : g.c - 1;
+  const int my_g = h * g.G + (row_ok ? my_row - div_g(g, my_row) * g.G : 0);
 
   // Q^T as B operands: lane (row col, half hh) holds Q[row][s*KS + hh*KL + i]
   typename M::frag qf[D / KS];
@@ -72,30 +74,45 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
 
   const int pk = g.keff << g.ps_log2;
   const int last_row = min(r0 + kFwdBM, rows_total) - 1;
-  const int t_lo = r0 / g.G;
-  const int nkeys = pk + last_row / g.G + 1;  // prior keys + chunk tokens up to the block's last
+  const int t_lo = div_g(g, r0);
+  const int nkeys = pk + div_g(g, last_row) + 1;  // prior keys + chunk tokens up to the block's last
   const int ntiles = (nkeys + BN - 1) / BN;
+  PageSlots<kPageCache> pages{page_tab};
+  pages.fill(g, a.pt, a.sel, h, (nkeys + (1 << g.ps_log2) - 1) >> g.ps_log2, tid, NT);
+  __syncthreads();
 
   const T* __restrict__ kp = (const T*)a.k;
   const T* __restrict__ vp = (const T*)a.v;
-  PairStages<T, D, BN, NT> kv{lds_k, lds_v};
-  // rows past the key list are clamped to its last key (finite data, masked below)
-  auto rows_from = [&](int j0) {
-    return [&, j0](int r) -> int64_t { return key_offset<D>(g, a.pt, a.sel, h, min(j0 + r, nkeys - 1)); };
+  KV kv{lds_k, lds_v};
+  // When a tile lies inside one page (page size a multiple of the tile), its
+  // rows are consecutive in the pool and one page lookup per tile suffices;
+  // rows past the key list then read the rest of that page (finite data,
+  // masked below).  Otherwise every row is looked up, clamped to the last key.
+  const bool tile_in_page = BN <= (1 << g.ps_log2);
+  auto load = [&](int j) {
+    if (tile_in_page) {
+      const int64_t base = pages.key_offset<D>(g, a.pt, a.sel, h, j * BN);
+      kv.load(j, kp, vp, tid, [base](int r) -> int64_t { return base + (int64_t)r * D; });
+    } else {
+      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t {
+        return pages.key_offset<D>(g, a.pt, a.sel, h, min(j * BN + r, nkeys - 1));
+      });
+    }
   };
+  const int vm_per_tile = KV::loads_per_tile(wave);
 
   float m_ref = -INFINITY, l = 0.f;  // running max (log2 domain) and this lane's partial sum
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
 
-  kv.load(0, kp, vp, tid, rows_from(0));
-  kv.commit(0, tid);
-  __syncthreads();
+  for (int j = 0; j < KV::PD && j < ntiles; ++j) load(j);
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * BN;
-    if (it + 1 < ntiles) kv.load((it + 1) & 1, kp, vp, tid, rows_from(j0 + BN));
-    const TL tk = kv.ta(it & 1), tv = kv.tb(it & 1);
+    kv.commit(it, min(KV::PD - 1, ntiles - 1 - it), vm_per_tile, tid);
+    __syncthreads();
+    if (it + KV::PD < ntiles) load(it + KV::PD);
+    const TL tk = kv.ta(it), tv = kv.tb(it);
 
     f32x16 sacc[BN / 32];
 #pragma unroll
@@ -111,7 +128,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int j = j0 + kb * 32 + acc_row(e, hh);
-          if (j >= nkeys || (j >= pk && j - pk > my_t)) sacc[kb][e] = -INFINITY;
+          sacc[kb][e] = (j >= nkeys || (j >= pk && j - pk > my_t)) ? -INFINITY : sacc[kb][e];
         }
     }
     float mx = -INFINITY;
@@ -132,7 +149,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
       m_ref = m_new;
     }
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
+    for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], a.scale_log2, -m_ref));
@@ -140,16 +157,12 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
         l += p;
       }
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
       for (int s = 0; s < 32 / KS; ++s) {
         const typename M::frag pf = M::pack(sacc[kb], s * KL);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) oacc[db] = M::mma(tv.frag_tr(kb, db, s, lane), pf, oacc[db]);
       }
-
-    if (it + 1 < ntiles) kv.commit((it + 1) & 1, tid);
-    __syncthreads();
+    }
   }
 
   l = wave_xor_sum(l, 32);

@@ -21,6 +21,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Geometry of one chunk step, as the kernels see it.
 struct Geo {
   int hq, hkv, G;          // query heads, kv heads, group size Hq/Hkv
+  uint64_t g_magic;        // ceil(2^40 / G): x / G == (x * g_magic) >> 40 for x < 2^24
   int c;                   // chunk tokens
   int n;                   // prior pages
   int keff;                // selected pages per kv-head
@@ -113,6 +114,13 @@ __device__ __forceinline__ int64_t key_offset(const Geo& g, const int32_t* __res
   return ((slot * g.hkv + h) * (int64_t)(1 << g.ps_log2) + row) * D;
 }
 
+// x / G for 0 <= x < 2^24 and G < 1024: the product stays below 2^64 and the
+// error of the rounded-up reciprocal, x * (g_magic - 2^40/G) / 2^40 < 2^-16,
+// stays below 1/G, so the floor is exact.
+__device__ __forceinline__ int div_g(const Geo& g, int x) {
+  return (int)(((uint64_t)(uint32_t)x * g.g_magic) >> 40);
+}
+
 // Workgroup b runs on XCD b % 8 (dispatch is round-robin over the 8 XCDs).
 // Map it to a work item so that each XCD gets a contiguous range of items,
 // whose K/V (or Q/dO) tiles then stay in that XCD's L2.
@@ -121,6 +129,30 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   if (b >= per * 8) return b;
   return (b % 8) * per + b / 8;
 }
+
+// Physical slots of the pages of a kv-head's key list J(h) -- the K_eff
+// selected pages, then the chunk's C/ps pages -- cached in LDS by a workgroup
+// (when they fit in CAP entries; otherwise read from global memory).
+template <int CAP> struct PageSlots {
+  int* tab;  // LDS, CAP entries
+  bool cached;
+
+  // all threads of the workgroup call this, then synchronise before use
+  __device__ __forceinline__ void fill(const Geo& g, const int32_t* __restrict__ pt,
+                                       const int32_t* __restrict__ sel, int h, int npages, int tid, int nt) {
+    cached = npages <= CAP;
+    if (cached)
+      for (int i = tid; i < npages; i += nt) tab[i] = pt[i < g.keff ? sel[h * g.keff + i] : g.n + i - g.keff];
+  }
+  template <int D>
+  __device__ __forceinline__ int64_t key_offset(const Geo& g, const int32_t* __restrict__ pt,
+                                                const int32_t* __restrict__ sel, int h, int jj) const {
+    if (!cached) return oomb::key_offset<D>(g, pt, sel, h, jj);
+    const int64_t slot = tab[jj >> g.ps_log2];
+    return ((slot * g.hkv + h) * (int64_t)(1 << g.ps_log2) + (jj & ((1 << g.ps_log2) - 1))) * D;
+  }
+};
+constexpr int kPageCache = 1024;
 
 // Warp-wide helpers (wave64).
 __device__ __forceinline__ float wave_xor_max(float v, int mask) { return fmaxf(v, __shfl_xor(v, mask, 64)); }

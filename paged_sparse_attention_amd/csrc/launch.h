@@ -22,6 +22,7 @@ inline Geo make_geo(const Shape& s) {
   g.hq = s.hq;
   g.hkv = s.hkv;
   g.G = s.hq / s.hkv;
+  g.g_magic = ((1ull << 40) + (uint64_t)g.G - 1) / (uint64_t)g.G;
   g.c = s.c;
   g.n = s.n;
   g.keff = s.keff;
@@ -41,6 +42,7 @@ SelectPlan select_plan(const Shape& s);
 
 struct BwdPlan {
   size_t off_dt;                  // Dt = rowsum(dO * O) per (head, token), fp32 [Hq][C]
+  size_t off_lse2;                // lse * log2(e) per (head, token), fp32 [Hq][C]
   size_t off_part_k, off_part_v;  // dK / dV partial sums of a row split, fp32 [splits][Hkv][nkeys][D]
   int splits;                     // workgroups sharing one key block's query rows
   size_t bytes;

@@ -140,31 +140,54 @@ template <int D, int BR, int NT> struct Stager {
   }
 };
 
-// Waits until this wave's direct-to-LDS loads have landed.
-__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Waits until at most n of this wave's vector-memory operations are still in
+// flight (direct-to-LDS loads included); n is clamped to the counter's range.
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  switch (n < 0 ? 0 : (n > 15 ? 15 : n)) {
+#define OOMB_WAIT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    OOMB_WAIT_CASE(0) OOMB_WAIT_CASE(1) OOMB_WAIT_CASE(2) OOMB_WAIT_CASE(3) OOMB_WAIT_CASE(4)
+    OOMB_WAIT_CASE(5) OOMB_WAIT_CASE(6) OOMB_WAIT_CASE(7) OOMB_WAIT_CASE(8) OOMB_WAIT_CASE(9)
+    OOMB_WAIT_CASE(10) OOMB_WAIT_CASE(11) OOMB_WAIT_CASE(12) OOMB_WAIT_CASE(13) OOMB_WAIT_CASE(14)
+    OOMB_WAIT_CASE(15)
+#undef OOMB_WAIT_CASE
+  }
+}
 
-// Two tensors with the same row addressing (K and V, or Q and dO), staged in
-// double-buffered tiles.  load(stage, ...) starts the copy of the next tiles;
-// commit(stage) finishes it for this thread (bf16: wait for the direct loads;
-// fp32: write the staged registers).  A barrier must follow commit before any
-// wave reads the stage.
-template <typename T, int D, int BR, int NT> struct PairStages {
+// Two tensors with the same row addressing (K and V, or Q and dO) streamed
+// through a ring of LDS tile slots.  bf16: three slots and two tiles in flight
+// ahead of the one in use, filled by direct-to-LDS loads; fp32: two slots, one
+// tile in flight staged in registers.  Use, per tile index j:
+//   load(j) for the first PD tiles; then for each j:
+//     commit(j, tiles_issued_after_j, extra) -- tile j has landed for this wave
+//     barrier                                 -- ... and for every wave
+//     load(j + PD) if it exists               -- refills the slot of tile j - 1
+//     read tiles ta(j), tb(j)
+template <typename T, int D, int BR, int NT> struct Ring {
   typedef Tile<T, D, BR> TL;
   static constexpr bool kDirect = sizeof(T) == 2;
-  T* pa;  // stage s of tensor a: pa + s * TL::ELEMS
+  static constexpr int NS = kDirect ? 3 : 2;  // slots
+  static constexpr int PD = NS - 1;           // tiles in flight ahead of the one in use
+  T* pa;                                      // slot s of tensor a: pa + s * TL::ELEMS
   T* pb;
-  Stager<D, BR, NT> sa, sb;
+  Stager<D, BR, NT> sa, sb;                   // fp32 only
 
-  __device__ __forceinline__ TL ta(int s) const { return TL{pa + s * TL::ELEMS}; }
-  __device__ __forceinline__ TL tb(int s) const { return TL{pb + s * TL::ELEMS}; }
+  __device__ __forceinline__ TL ta(int j) const { return TL{pa + (j % NS) * TL::ELEMS}; }
+  __device__ __forceinline__ TL tb(int j) const { return TL{pb + (j % NS) * TL::ELEMS}; }
+
+  // direct loads one wave issues per tile (both tensors)
+  __device__ static __forceinline__ int loads_per_tile(int wave) {
+    if constexpr (kDirect) return 2 * ((TL::BLOCKS - wave + NT / 64 - 1) / (NT / 64));
+    else return 0;
+  }
 
   template <typename OffFn>
-  __device__ __forceinline__ void load(int stage, const T* __restrict__ srca, const T* __restrict__ srcb, int tid,
+  __device__ __forceinline__ void load(int j, const T* __restrict__ srca, const T* __restrict__ srcb, int tid,
                                        OffFn off) {
     if constexpr (kDirect) {
       const int wave = tid >> 6, lane = tid & 63;
-      T* da = pa + stage * TL::ELEMS;
-      T* db = pb + stage * TL::ELEMS;
+      T* da = pa + (j % NS) * TL::ELEMS;
+      T* db = pb + (j % NS) * TL::ELEMS;
       for (int blk = wave; blk < TL::BLOCKS; blk += NT / 64) {
         const int q = blk * 64 + lane;
         const int r = q / TL::SLOTS, p = q % TL::SLOTS;
@@ -178,14 +201,22 @@ template <typename T, int D, int BR, int NT> struct PairStages {
       sb.load((const float*)srcb, tid, off);
     }
   }
-  __device__ __forceinline__ void commit(int stage, int tid) {
+  // tile j is in LDS as far as this thread is concerned; `newer` tiles were
+  // issued after it, each costing `vm_per_tile` vector-memory operations
+  __device__ __forceinline__ void commit(int j, int newer, int vm_per_tile, int tid) {
     if constexpr (kDirect) {
-      wait_lds_loads();
+      wait_vmem_le(newer * vm_per_tile);
     } else {
-      sa.store(Tile<float, D, BR>{(float*)pa + stage * TL::ELEMS}, tid);
-      sb.store(Tile<float, D, BR>{(float*)pb + stage * TL::ELEMS}, tid);
+      sa.store(Tile<float, D, BR>{(float*)pa + (j % NS) * TL::ELEMS}, tid);
+      sb.store(Tile<float, D, BR>{(float*)pb + (j % NS) * TL::ELEMS}, tid);
     }
   }
 };
+
+// One 32-bit value per lane straight from global memory to LDS (lane l writes
+// dst[l]); lanes outside exec write nothing.
+__device__ __forceinline__ void load_lds_dword(const float* src, float* dst_wave_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst_wave_base, 4, 0, 0);
+}
 
 }  // namespace oomb
