@@ -132,13 +132,13 @@ template <int D> struct KeyStore<float, D> {  // registers
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(kv_waves<T>() * 64, sizeof(T) == 2 ? 2 : 1) void dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) {
   typedef Mma<T> M;
   constexpr int BM = kv_bm<T, D>(), KEYS = kv_keys<T>(), NW = kv_waves<T>(), NT = NW * 64;
   typedef Tile<T, D, BM> TL;
   constexpr int KS = M::KS, KL = M::KL;
   constexpr bool kKeysInLds = sizeof(T) == 2;
-  typedef Ring<T, D, BM, NT> QD;
+  typedef Ring<T, D, BM, NT, 2> QD;  // two slots: two workgroups fit a CU
   __shared__ __attribute__((aligned(16))) T lds_q[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_d[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_keys[kKeysInLds ? KeyStore<__bf16, D>::TK::ELEMS : 1];
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, sizeof(T) == 2 ? 2 : 1) void dk
   const int kblk = (item / plan.splits) % plan.nkb;
   const int sp = item % plan.splits;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int pk = g.keff << g.ps_log2;
   const int nkeys = pk + g.c;
@@ -242,23 +242,32 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, sizeof(T) == 2 ? 2 : 1) void dk
       // element e of a lane: query token tb + acc_row(e, hh) of head gi, key my_key
       const int tb = t0 + rb * 32;
       const bool full = tb + 32 <= g.c && wave_keys_ok && (wave_prior || tb >= wave_last - pk);
+      // rows acc_row(4i + j, hh) = 8i + 4hh + j: four consecutive rows per i
       if (full) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = rb * 32 + acc_row(e, hh);
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -ml[r]));
-          sacc[e] = p;
-          pacc[e] = p * (pacc[e] - md[r]);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ml + rb * 32 + 8 * i + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(md + rb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]));
+            sacc[4 * i + j] = p;
+            pacc[4 * i + j] = p * (pacc[4 * i + j] - d4[j]);
+          }
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = rb * 32 + acc_row(e, hh);
-          const int t = tb + acc_row(e, hh);
-          const bool vis = key_ok && t < g.c && my_u <= t;  // my_u < 0 for prior keys
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -ml[r])) : 0.f;
-          sacc[e] = p;
-          pacc[e] = p * (pacc[e] - md[r]);
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ml + rb * 32 + 8 * i + 4 * hh);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(md + rb * 32 + 8 * i + 4 * hh);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t = tb + 8 * i + 4 * hh + j;
+            const bool vis = key_ok && t < g.c && my_u <= t;  // my_u < 0 for prior keys
+            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], a.scale_log2, -l4[j])) : 0.f;
+            sacc[4 * i + j] = p;
+            pacc[4 * i + j] = p * (pacc[4 * i + j] - d4[j]);
+          }
         }
       }
 #pragma unroll
@@ -342,16 +351,16 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ, query-major.
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;
+constexpr int kDqWaves = 4;
 constexpr int kDqBM = 32 * kDqWaves;  // query rows per workgroup
 template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 64 : 32; }  // keys per tile
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(BwdArgs a) {
   typedef Mma<T> M;
   constexpr int BN = dq_bn<T>();
   constexpr int NT = kDqWaves * 64;
-  typedef Ring<T, D, BN, NT> KV;
+  typedef Ring<T, D, BN, NT, 2> KV;  // two slots: two workgroups fit a CU
   typedef typename KV::TL TL;
   constexpr int KS = M::KS, KL = M::KL;
   __shared__ __attribute__((aligned(16))) T lds_k[KV::NS * TL::ELEMS];
@@ -365,7 +374,7 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
   const int h = item / nrb;
   const int r0 = (nrb - 1 - item % nrb) * kDqBM;  // later (heavier) row blocks first
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
   const int my_row = r0 + wave * 32 + col;
   const bool row_ok = my_row < rows_total;

@@ -104,15 +104,23 @@ __global__ __launch_bounds__(256) void qmean_partial_kernel(const T* __restrict_
   }
 }
 
-// Stage 2: qbar[h][:] = (sum over blocks of partial) / (C * G).  One workgroup.
+// Stage 2: qbar[h][:] = (sum over blocks of partial) / (C * G).  A workgroup
+// takes 64 output columns; its four waves sum every fourth block, then add their
+// four sums in a fixed order.
 __global__ __launch_bounds__(256) void qmean_final_kernel(const float* __restrict__ partial, int nblk,
                                                           int width, float inv_count,
                                                           float* __restrict__ qbar) {
-  for (int o = threadIdx.x; o < width; o += 256) {
-    float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += partial[(int64_t)b * width + o];
-    qbar[o] = s * inv_count;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int o = blockIdx.x * 64 + lane;
+  float s = 0.f;
+  if (o < width) {
+#pragma unroll 8
+    for (int b = wave; b < nblk; b += 4) s += partial[(int64_t)b * width + o];
   }
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && o < width) qbar[o] = (((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]) * inv_count;
 }
 
 // ---------------------------------------------------------------------------
@@ -308,7 +316,7 @@ static hipError_t select_t(const Shape& s, const SelectPlan& p, const void* q, c
   }
   {
     Traced tr(st, "qmean_final_kernel");
-    hipLaunchKernelGGL(qmean_final_kernel, dim3(1), dim3(256), 0, st, (const float*)partial, p.nblk, width,
+    hipLaunchKernelGGL(qmean_final_kernel, dim3((width + 63) / 64), dim3(256), 0, st, (const float*)partial, p.nblk, width,
                        1.0f / ((float)s.c * (float)(s.hq / s.hkv)), qbar);
   }
   const int ppb = 16;

@@ -67,16 +67,21 @@ template <int D, int BR> struct Tile<__bf16, D, BR> {
       __builtin_amdgcn_global_load_lds((gbl_void*)(src + off(r) + c * VEC), (lds_void*)(rm + b * 512), 16, 0, 0);
     }
   }
+  // (2s + hh) ^ flip(row) == 2s + (hh ^ flip(row)): s only adds an immediate offset
   __device__ __forceinline__ bf16x8 frag_rm(int row, int s, int hh) const {
-    return *reinterpret_cast<const bf16x8*>(rm + row * RS + ((2 * s + hh) ^ flip(row)) * VEC);
+    return *reinterpret_cast<const bf16x8*>(rm + row * RS + (hh ^ flip(row)) * VEC + s * 2 * VEC);
   }
   __device__ __forceinline__ bf16x8 frag_tr(int rb, int cb, int s, int lane) const {
+    // lane (g, j) = (lane / 16, lane % 16) reads row rb*32 + 16s + rl (+ 8) and
+    // chunk 4cb + cl; rl < 8, so flip() is 0 on the first row and 1 on the
+    // second, and rb, s and cb only add immediate offsets
     const int g = lane >> 4, j = lane & 15;
-    const int row = rb * 32 + 16 * s + 4 * (g >> 1) + (j >> 2);
-    const int c = 4 * cb + 2 * (g & 1) + ((j & 3) >> 1);
+    const int rl = 4 * (g >> 1) + (j >> 2);
+    const int cl = 2 * (g & 1) + ((j & 3) >> 1);
     const int half = (j & 1) * 4;
-    const T* p0 = rm + row * RS + (c ^ flip(row)) * VEC + half;
-    const T* p1 = rm + (row + 8) * RS + (c ^ flip(row + 8)) * VEC + half;
+    const int fixed = (rb * 32 + 16 * s) * RS + 4 * cb * VEC;
+    const T* p0 = rm + fixed + rl * RS + cl * VEC + half;
+    const T* p1 = rm + fixed + (rl + 8) * RS + (cl ^ flip(8)) * VEC + half;
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p1);
     bf16x8 f;
@@ -163,10 +168,10 @@ __device__ __forceinline__ void wait_vmem_le(int n) {
 //     barrier                                 -- ... and for every wave
 //     load(j + PD) if it exists               -- refills the slot of tile j - 1
 //     read tiles ta(j), tb(j)
-template <typename T, int D, int BR, int NT> struct Ring {
+template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2> struct Ring {
   typedef Tile<T, D, BR> TL;
   static constexpr bool kDirect = sizeof(T) == 2;
-  static constexpr int NS = kDirect ? 3 : 2;  // slots
+  static constexpr int NS = NSLOTS;           // slots
   static constexpr int PD = NS - 1;           // tiles in flight ahead of the one in use
   T* pa;                                      // slot s of tensor a: pa + s * TL::ELEMS
   T* pb;

@@ -461,3 +461,44 @@ def pin_bwd_row_additivity(ora):
 
 
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
+
+
+def _golden_value(v):
+    """A fixture entry: a number, or a closed form in sqrt, ln and rationals."""
+    if isinstance(v, (int, float)):
+        return float(v)
+    return float(eval(v, {"__builtins__": {}}, {"sqrt": math.sqrt, "ln": math.log}))
+
+
+def pin_golden_two_key_step(ora):
+    """The hand-worked step in tests/golden/two_key_step.json: forward and backward."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "two_key_step.json")
+    with open(path) as f:
+        gd = json.load(f)
+    vec = lambda name: np.array([_golden_value(v) for v in gd[name]])
+    sh = gd["shape"]
+    p = Problem(hq=sh["hq"], hkv=sh["hkv"], d=sh["d"], ps=sh["ps"], c=sh["c"], n=sh["n"], k=sh["k"], dtype="f64")
+    pt = np.array(gd["page_table"], dtype=np.int32)
+    sel = np.array(gd["sel"], dtype=np.int32)
+    kp = np.zeros((2, 1, 1, 2))
+    vp = np.zeros((2, 1, 1, 2))
+    kp[pt[0], 0, 0], vp[pt[0], 0, 0] = vec("k_prior"), vec("v_prior")
+    kp[pt[1], 0, 0], vp[pt[1], 0, 0] = vec("k_own"), vec("v_own")
+    q = vec("q").reshape(1, 1, 2)
+    do = vec("dO").reshape(1, 1, 2)
+    ex = gd["expected"]
+    o, lse = ora.fwd(p, q, kp, vp, pt, sel)
+    close(lse, [_golden_value(ex["lse"])], 1e-15, "golden LSE")
+    close(o[0], [_golden_value(v) for v in ex["o"]], 1e-14, "golden O")
+    dq, dk, dv = ora.bwd(p, q, kp, vp, pt, sel, do)
+    ev = lambda name: [_golden_value(v) for v in ex[name]]
+    close(dq[0], ev("dq"), 1e-14, "golden dQ")
+    close(dk[0, 0], ev("dk_prior"), 1e-14, "golden dK prior")
+    close(dk[0, 1], ev("dk_own"), 1e-14, "golden dK own")
+    close(dv[0, 0], ev("dv_prior"), 1e-14, "golden dV prior")
+    close(dv[0, 1], ev("dv_own"), 1e-14, "golden dV own")
+
+
+PINS["pin_golden_two_key_step"] = pin_golden_two_key_step
