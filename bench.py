@@ -121,7 +121,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sparse-256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="chunk tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=1536, help="chunk tokens in the oracle's timed sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
           for (int j = 0; j < 4; ++j) {
             const int t = tb + 8 * i + 4 * hh + j;
             const bool vis = key_ok && t < g.c && my_u <= t;  // my_u < 0 for prior keys
-            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[4 * i + j], a.scale_log2, -l4[j])) : 0.f;
+            const float p = __builtin_amdgcn_exp2f(vis ? fmaf(sacc[4 * i + j], a.scale_log2, -l4[j]) : -INFINITY);
             sacc[4 * i + j] = p;
             pacc[4 * i + j] = p * (pacc[4 * i + j] - d4[j]);
           }
@@ -437,12 +437,21 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(BwdArgs a) {
         sacc = M::mma(tk.frag_rm(kb * 32 + col, s, hh), qf[s], sacc);
         pacc = M::mma(tv.frag_rm(kb * 32 + col, s, hh), df[s], pacc);
       }
+      // invisible pairs take exponent -inf (weight 0), so exp2 runs unconditionally
+      if (masked) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = j0 + kb * 32 + acc_row(e, hh);
-        const bool vis = !masked || (j < nkeys && (j < pk || j - pk <= my_t));
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -my_lse)) : 0.f;
-        pacc[e] = p * (pacc[e] - my_dt);
+        for (int e = 0; e < 16; ++e) {
+          const int j = j0 + kb * 32 + acc_row(e, hh);
+          const bool vis = j < nkeys && (j < pk || j - pk <= my_t);
+          const float p = __builtin_amdgcn_exp2f(vis ? fmaf(sacc[e], a.scale_log2, -my_lse) : -INFINITY);
+          pacc[e] = p * (pacc[e] - my_dt);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[e], a.scale_log2, -my_lse));
+          pacc[e] = p * (pacc[e] - my_dt);
+        }
       }
 #pragma unroll
       for (int s = 0; s < 32 / KS; ++s) {

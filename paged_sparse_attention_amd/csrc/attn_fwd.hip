@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   const int h = item / nrb;
   const int r0 = (nrb - 1 - item % nrb) * kFwdBM;  // later (heavier) row blocks first
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
   const int my_row = r0 + wave * 32 + col;
   const bool row_ok = my_row < rows_total;
