@@ -149,8 +149,10 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   const KvPlan plan = kv_plan(g, KEYS);
   const int item = xcd_remap(blockIdx.x, plan.nkb * plan.splits * g.hkv);
   const int h = item / (plan.nkb * plan.splits);
-  const int kblk = (item / plan.splits) % plan.nkb;
-  const int sp = item % plan.splits;
+  // key blocks vary fastest: the workgroups that run together on one XCD
+  // stream the same share of query rows, which then stays in its L2
+  const int kblk = item % plan.nkb;
+  const int sp = (item / plan.nkb) % plan.splits;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
