@@ -114,6 +114,48 @@ def cpu_baseline(p, seed, x, tokens):
             "seconds": t_sel + t_rows, "rep_setup_seconds": t_setup}
 
 
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+    counter readings convert the attention kernels' readings to bytes."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
+
+
+SOURCE_DIRS = ("paged_sparse_attention_amd/csrc", "include")
+
+
+def source_digest():
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in SOURCE_DIRS:
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            if name.endswith((".hip", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(ROOT, d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the counter summary in profiles/,
+    or None when there is none or the sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,7 +164,12 @@ def main():
     ap.add_argument("--workload", default="sparse-256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="chunk tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by kv-head across GPUs by design but no multi-GPU code is built", file=sys.stderr)
@@ -188,11 +235,12 @@ def main():
         peak = PEAK_BF16_TFLOPS if p.dtype == "bf16" else PEAK_FP32_TFLOPS
         achieved = work / avg_s / 1e12
         roof = {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": None, "work_per_launch": work}
+                "frac": achieved / peak, "traffic": measured_traffic(dominant, args.workload), "work_per_launch": work}
     else:
         achieved = work / avg_s / 1e9
         roof = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "work_per_launch": work}
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(dominant, args.workload),
+                "work_per_launch": work}
     for n, kv in kernels.items():
         b, w, u = kernel_work(p, n)
         s = kv["avg_ms"] / 1e3
