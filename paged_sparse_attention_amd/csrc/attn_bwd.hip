@@ -353,16 +353,16 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ, query-major.
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 4;
+constexpr int kDqWaves = 8;
 constexpr int kDqBM = 32 * kDqWaves;  // query rows per workgroup
-template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 64 : 32; }  // keys per tile
+template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 128 : 32; }  // keys per tile
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDqWaves * 64, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
   typedef Mma<T> M;
   constexpr int BN = dq_bn<T>();
   constexpr int NT = kDqWaves * 64;
-  typedef Ring<T, D, BN, NT, 2> KV;  // two slots: two workgroups fit a CU
+  typedef Ring<T, D, BN, NT, 2> KV;  // two slots of 128 keys fill most of the LDS
   typedef typename KV::TL TL;
   constexpr int KS = M::KS, KL = M::KL;
   __shared__ __attribute__((aligned(16))) T lds_k[KV::NS * TL::ELEMS];
