@@ -29,6 +29,10 @@ SMALL = {
     "extra-slots": (28, Problem(hq=6, hkv=2, d=64, ps=32, c=64, n=10, k=4, n_slots=30)),
     "scale-override-fp32": (29, Problem(hq=4, hkv=2, d=64, ps=16, c=32, n=8, k=3, dtype="f32", scale=0.05)),
     "d64-bf16-g7": (30, Problem(hq=14, hkv=2, d=64, ps=16, c=112, n=31, k=9)),
+    # more key pages than the kernels' LDS page-slot cache holds (1024): slots
+    # are then read from the page table for every tile
+    "uncached-pages-dense": (31, Problem(hq=4, hkv=1, d=64, ps=16, c=32, n=1100, k=2000)),
+    "uncached-pages-topk": (32, Problem(hq=8, hkv=2, d=128, ps=16, c=64, n=1500, k=1100)),
 }
 
 FULL = ["dense-32k", "sparse-256k", "sparse-1m", "sparse-4m"]
