@@ -52,32 +52,47 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Dt = rowsum(dO * O) and lse in log2 units, one row per group of D/VEC lanes.
+// Dt = rowsum(dO * O) and lse in log2 units, one row per group of D/VEC lanes;
+// a thread takes kDtRows rows, their loads issued together.
 // ---------------------------------------------------------------------------
+constexpr int kDtRows = 4;
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dt_kernel(BwdArgs a) {
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int LPR = D / VEC;  // lanes per row (power of two, <= 32)
+  constexpr int RPB = 256 / LPR;  // rows per block and pass
   const int rows = a.g.c * a.g.hq;
   const int lane_in_row = threadIdx.x % LPR;
-  const int row = blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  float s = 0.f;
-  if (row < rows) {
-    const int64_t off = (int64_t)row * D + lane_in_row * VEC;
-    const f32x4 ro = *reinterpret_cast<const f32x4*>((const T*)a.o + off);
-    const f32x4 rd = *reinterpret_cast<const f32x4*>((const T*)a.dout + off);
-    const T* po = reinterpret_cast<const T*>(&ro);
-    const T* pd = reinterpret_cast<const T*>(&rd);
+  const int row0 = blockIdx.x * (RPB * kDtRows) + threadIdx.x / LPR;
+  f32x4 ro[kDtRows], rd[kDtRows];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) s += (float)po[i] * (float)pd[i];
+  for (int k = 0; k < kDtRows; ++k) {
+    const int row = row0 + k * RPB;
+    if (row < rows) {
+      const int64_t off = (int64_t)row * D + lane_in_row * VEC;
+      ro[k] = *reinterpret_cast<const f32x4*>((const T*)a.o + off);
+      rd[k] = *reinterpret_cast<const f32x4*>((const T*)a.dout + off);
+    }
   }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) s = wave_xor_sum(s, m);
-  if (row < rows && lane_in_row == 0) {
-    const int t = row / a.g.hq, g = row % a.g.hq;  // row = t * Hq + g
-    const int64_t i = (int64_t)g * a.g.c + t;
-    a.dt[i] = s;
-    a.lse2[i] = a.lse[i] * kLog2e;
+  for (int k = 0; k < kDtRows; ++k) {
+    const int row = row0 + k * RPB;
+    float s = 0.f;
+    if (row < rows) {
+      const T* po = reinterpret_cast<const T*>(&ro[k]);
+      const T* pd = reinterpret_cast<const T*>(&rd[k]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s += (float)po[i] * (float)pd[i];
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) s = wave_xor_sum(s, m);
+    if (row < rows && lane_in_row == 0) {
+      const int t = row / a.g.hq, g = row % a.g.hq;  // row = t * Hq + g
+      const int64_t i = (int64_t)g * a.g.c + t;
+      a.dt[i] = s;
+      a.lse2[i] = a.lse[i] * kLog2e;
+    }
   }
 }
 
@@ -353,15 +368,15 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ, query-major.
 // ---------------------------------------------------------------------------
-constexpr int kDqWaves = 8;
-constexpr int kDqBM = 32 * kDqWaves;  // query rows per workgroup
+template <typename T> constexpr int dq_waves() { return sizeof(T) == 2 ? 8 : 4; }
+template <typename T> constexpr int dq_bm() { return 32 * dq_waves<T>(); }  // query rows per workgroup
 template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 128 : 32; }  // keys per tile
 
 template <typename T, int D>
-__global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   typedef Mma<T> M;
   constexpr int BN = dq_bn<T>();
-  constexpr int NT = kDqWaves * 64;
+  constexpr int NT = dq_waves<T>() * 64, BM = dq_bm<T>();
   typedef Ring<T, D, BN, NT, 2> KV;  // two slots of 128 keys fill most of the LDS
   typedef typename KV::TL TL;
   constexpr int KS = M::KS, KL = M::KL;
@@ -371,10 +386,10 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
 
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
-  const int nrb = (rows_total + kDqBM - 1) / kDqBM;
+  const int nrb = (rows_total + BM - 1) / BM;
   const int item = xcd_remap(blockIdx.x, nrb * g.hkv);
   const int h = item / nrb;
-  const int r0 = (nrb - 1 - item % nrb) * kDqBM;  // later (heavier) row blocks first
+  const int r0 = (nrb - 1 - item % nrb) * BM;  // later (heavier) row blocks first
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(kDqWaves * 64) void dq_kernel(BwdArgs a) {
   const float my_dt = row_ok ? a.dt[(int64_t)my_g * g.c + my_t] : 0.f;
 
   const int pk = g.keff << g.ps_log2;
-  const int last_row = min(r0 + kDqBM, rows_total) - 1;
+  const int last_row = min(r0 + BM, rows_total) - 1;
   const int t_lo = div_g(g, r0);
   const int nkeys = pk + div_g(g, last_row) + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
@@ -505,7 +520,8 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const int rows = a.g.c * a.g.hq;
   {
     Traced tr(st, "dt_kernel");
-    hipLaunchKernelGGL((dt_kernel<T, D>), dim3((rows + 256 / LPR - 1) / (256 / LPR)), dim3(256), 0, st, a);
+    const int per_block = (256 / LPR) * kDtRows;
+    hipLaunchKernelGGL((dt_kernel<T, D>), dim3((rows + per_block - 1) / per_block), dim3(256), 0, st, a);
   }
   const KvPlan kp = kv_plan(a.g, kv_keys<T>());
   {
@@ -521,8 +537,8 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const int qrows = a.g.c * a.g.G;
   {
     Traced tr(st, "dq_kernel");
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(((qrows + kDqBM - 1) / kDqBM) * a.g.hkv), dim3(kDqWaves * 64), 0,
-                       st, a);
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(((qrows + dq_bm<T>() - 1) / dq_bm<T>()) * a.g.hkv),
+                       dim3(dq_waves<T>() * 64), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ inline Geo make_geo(const Shape& s) {
   return g;
 }
 
-constexpr int kQmeanBlocks = 128;  // token blocks of the chunk-mean-query reduction
+constexpr int kQmeanBlocks = 256;  // token blocks of the chunk-mean-query reduction
 
 struct SelectPlan {
   int tpb, nblk;                                   // tokens per block, blocks

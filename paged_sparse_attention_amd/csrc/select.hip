@@ -80,19 +80,23 @@ __global__ __launch_bounds__(256) void qmean_partial_kernel(const T* __restrict_
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
   if (tg < TG) {
-    for (int t = t0 + tg; t < t1; t += TG)
-      for (int gi = 0; gi < G; ++gi) {
-        const T* src = q + ((int64_t)t * hq + h * G + gi) * D + d0;
-        if constexpr (sizeof(T) == 2) {
-          const bf16x8 v = *reinterpret_cast<const bf16x8*>(src);
+    // (token, head) pairs of the block, flattened so that the unrolled loop
+    // keeps several independent loads in flight
+    const int n = (t1 - t0) * G;
+#pragma unroll 8
+    for (int k = tg; k < n; k += TG) {
+      const int t = t0 + k / G, gi = k % G;
+      const T* src = q + ((int64_t)t * hq + h * G + gi) * D + d0;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(src);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] += (float)v[i];
-        } else {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(src);
+        for (int i = 0; i < VEC; ++i) acc[i] += (float)v[i];
+      } else {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-          for (int i = 0; i < VEC; ++i) acc[i] += v[i];
-        }
+        for (int i = 0; i < VEC; ++i) acc[i] += v[i];
       }
+    }
 #pragma unroll
     for (int i = 0; i < VEC; ++i) red[tg * hkv * D + col * VEC + i] = acc[i];
   }
