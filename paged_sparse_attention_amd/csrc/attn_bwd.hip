@@ -9,16 +9,16 @@
 // Kernels, in stream order:
 //   1. dt_kernel:   Dt[g][t] = dO[t][g] . O[t][g]                 (HBM-bound)
 //   2. dkdv_kernel: key-major.  A workgroup owns 128 keys of one kv-head's key
-//      list (4 waves x 32 keys; V in registers, K in LDS) and walks a share of
-//      the query rows that see them in tiles of 64 rows, recomputing
-//      S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
-//      dK^T += Q^T dS (dO^T and Q^T read transposed from the row-major LDS
-//      tiles).  When the rows are split over several workgroups for load
-//      balance, each writes its partial sums to the workspace.
+//      list (4 waves x 32 keys; V in registers, K in LDS; two workgroups per
+//      CU) and walks a share of the query rows that see them, head by head in
+//      tiles of 32 rows, recomputing S = Q K^T and dP = dO V^T on MFMA, then
+//      dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the
+//      row-major LDS tiles).  When the rows are split over several workgroups
+//      for load balance, each writes its partial sums to the workspace.
 //   3. kv_reduce_kernel (only with a row split): dk_pool/dv_pool += the sum of
 //      the partials, in split order.
-//   4. dq_kernel:   query-major, like the forward: S^T and dP^T per key tile,
-//      dQ^T += K^T dS^T, written once per row.
+//   4. dq_kernel:   query-major, like the forward: S^T and dP^T per 32-key
+//      block of a K/V tile, dQ^T += K^T dS^T, written once per row.
 // Every (slot, kv-head, row) of the gradient pools is changed by exactly one
 // thread, once, in a fixed order: no atomics, bitwise reproducible, and slots
 // outside the selected and chunk pages are never touched.  P and dS are
