@@ -185,3 +185,49 @@ class Oracle:
             row[h, :pk] = jj[:pk] % p.ps
             row[h, pk:] = (jj[pk:] - pk) % p.ps
         return slot, row
+
+    # --- a whole sequence, chunk by chunk ------------------------------------
+    def sequence(self, s, x, sels=None):
+        """Chunk-recurrent attention of one layer over a whole sequence (the
+        OOMB page, technical summary, section 2: chunk-recurrent training with
+        page-level sparse attention over a paged KV cache).
+
+        Forward, chunks in order: chunk i (a chunk step whose prior pages are the
+        initial context and chunks 0 .. i-1) scores those pages by their
+        representative vectors, takes its top-K, and attends.  Backward, chunks
+        in reverse order: each chunk reuses its selection and adds its dK/dV
+        into the pools shared by the whole sequence.  `s` is a synth.Sequence;
+        `sels`, if given, replaces the chunks' own selections.
+
+        Returns a dict: per chunk lists sel, scores, o [c*hq][d], lse [c*hq],
+        dq [c*hq][d]; pool-shaped dk, dv [slots][hkv][ps][d] (the sums).
+        """
+        last = s.step(s.chunks - 1)
+        pt = np.ascontiguousarray(x["page_table"], dtype=np.int32)
+        # a page's representative vector depends only on its keys: those of all
+        # pages at once, for the chunks to read their prior pages from
+        rep = self.rep(last, x["k_pool"], pt, 0, s.pages)
+        out = {"sel": [], "scores": [], "o": [], "lse": [], "dq": [None] * s.chunks}
+        for i in range(s.chunks):
+            p = s.step(i)
+            q = np.ascontiguousarray(x["q"][i])
+            sc = self.scores(p, self.qmean(p, q), rep[:p.n]) if p.n > 0 else np.zeros((p.hkv, 0))
+            sel = self.select(p, sc) if sels is None else np.asarray(sels[i], dtype=np.int32).reshape(p.hkv, p.keff)
+            o, lse = self.fwd(p, q, x["k_pool"], x["v_pool"], pt, sel)
+            out["sel"].append(sel)
+            out["scores"].append(sc)
+            out["o"].append(o)
+            out["lse"].append(lse)
+        dk = np.zeros((last.slots, s.hkv, s.ps, s.d), dtype=np.float64)
+        dv = np.zeros_like(dk)
+        for i in reversed(range(s.chunks)):
+            p = s.step(i)
+            dq, dki, dvi = self.bwd(p, np.ascontiguousarray(x["q"][i]), x["k_pool"], x["v_pool"], pt, out["sel"][i],
+                                    np.ascontiguousarray(x["do"][i]))
+            slot, row = self.key_slots(p, pt, out["sel"][i])
+            for h in range(p.hkv):
+                np.add.at(dk, (slot[h], h, row[h]), dki[h])
+                np.add.at(dv, (slot[h], h, row[h]), dvi[h])
+            out["dq"][i] = dq
+        out["dk"], out["dv"] = dk, dv
+        return out

@@ -155,6 +155,53 @@ def make_inputs(p: Problem, seed: int) -> dict:
     }
 
 
+@dataclasses.dataclass(frozen=True)
+class Sequence:
+    """A whole sequence of one layer processed chunk by chunk: n0 initial pages
+    of context, then `chunks` chunks of c tokens; chunk i has n0 + i*c/ps prior
+    pages.  The pools hold every page of the sequence."""
+    hq: int
+    hkv: int
+    d: int
+    ps: int
+    c: int
+    chunks: int
+    k: int
+    n0: int = 0
+    dtype: str = "bf16"
+    scale: float = 0.0
+
+    @property
+    def chunk_pages(self) -> int:
+        return self.c // self.ps
+
+    @property
+    def pages(self) -> int:
+        return self.n0 + self.chunks * self.chunk_pages
+
+    def step(self, i: int) -> Problem:
+        """The chunk step of chunk i (its pools span the whole sequence)."""
+        return Problem(self.hq, self.hkv, self.d, self.ps, self.c, self.n0 + i * self.chunk_pages, self.k,
+                       self.dtype, n_slots=self.pages, scale=self.scale)
+
+    def pairs(self) -> int:
+        return sum(self.step(i).pairs() for i in range(self.chunks))
+
+
+def make_sequence_inputs(s: Sequence, seed: int) -> dict:
+    """Inputs of a whole sequence: pools and page table of every page, and
+    Q / dO of every chunk ([chunks][c][hq][d])."""
+    last = s.step(s.chunks - 1)
+    pt = page_table(last, seed)
+    return {
+        "page_table": pt,
+        "q": tensor(seed, S_Q, (s.chunks, s.c, s.hq, s.d), s.dtype),
+        "k_pool": pool(last, seed, "k", pt),
+        "v_pool": pool(last, seed, "v", pt),
+        "do": tensor(seed, S_DO, (s.chunks, s.c, s.hq, s.d), s.dtype),
+    }
+
+
 def canary(p: Problem, seed: int, which: str) -> np.ndarray:
     """Seeded fp32 prefill for a gradient pool (so untouched slots can be checked)."""
     return tensor(seed, S_DK0 if which == "k" else S_DV0, (p.slots, p.hkv, p.ps, p.d), "f32")

@@ -460,6 +460,72 @@ def pin_bwd_row_additivity(ora):
     close(qb, q[B], 0.0, "dq rows")
 
 
+def _seq(**kw):
+    base = dict(hq=4, hkv=2, d=16, ps=4, c=8, chunks=3, k=3, n0=2, dtype="f64")
+    base.update(kw)
+    return synth.Sequence(**base)
+
+
+def pin_sequence_dense_equals_one_long_chunk(ora):
+    """With every earlier page selected, chunk-recurrent attention over a
+    sequence is causal attention over the whole sequence: the same as one
+    chunk step whose chunk is all the chunks' tokens (its own prior pages being
+    the initial context).  Forward and backward, pool by pool."""
+    s = _seq(k=1000)
+    x = synth.make_sequence_inputs(s, 41)
+    r = ora.sequence(s, x)
+    big = Problem(hq=s.hq, hkv=s.hkv, d=s.d, ps=s.ps, c=s.chunks * s.c, n=s.n0, k=1000, dtype=s.dtype,
+                  n_slots=s.pages)
+    q = x["q"].reshape(s.chunks * s.c, s.hq, s.d)
+    do = x["do"].reshape(s.chunks * s.c, s.hq, s.d)
+    sel = np.tile(np.arange(s.n0, dtype=np.int32), (s.hkv, 1))
+    o, lse = ora.fwd(big, q, x["k_pool"], x["v_pool"], x["page_table"], sel)
+    dq, dk, dv = ora.bwd(big, q, x["k_pool"], x["v_pool"], x["page_table"], sel, do)
+    rows = s.c * s.hq
+    for i in range(s.chunks):
+        close(r["o"][i], o[i * rows:(i + 1) * rows], 1e-12, f"O chunk {i}")
+        close(r["lse"][i], lse[i * rows:(i + 1) * rows], 1e-12, f"LSE chunk {i}")
+        close(r["dq"][i], dq[i * rows:(i + 1) * rows], 1e-12, f"dQ chunk {i}")
+    dkp, dvp = _pool_grads(ora, big, x, sel, dk, dv)
+    close(r["dk"], dkp, 1e-12, "dK pool")
+    close(r["dv"], dvp, 1e-12, "dV pool")
+
+
+def pin_sequence_selection_by_chunk(ora):
+    """Chunk i picks among exactly the pages before it (initial context and
+    chunks 0 .. i-1): its pages are numpy's top-K of (the chunk's mean query
+    over tokens and group heads) . (page key means), ties to the lower page,
+    listed ascending."""
+    s = _seq(k=3, chunks=4, n0=2)
+    x = synth.make_sequence_inputs(s, 42)
+    r = ora.sequence(s, x)
+    kseq = logical_seq(s.step(s.chunks - 1), x["k_pool"], x["page_table"])   # [hkv][pages*ps][d]
+    page_mean = kseq.reshape(s.hkv, s.pages, s.ps, s.d).mean(axis=2)
+    G = s.hq // s.hkv
+    for i in range(s.chunks):
+        n = s.n0 + i * s.c // s.ps
+        keff = min(s.k, n)
+        for h in range(s.hkv):
+            qbar = x["q"][i][:, h * G:(h + 1) * G, :].mean(axis=(0, 1))
+            sc = page_mean[h, :n] @ qbar
+            order = sorted(range(n), key=lambda m: (-sc[m], m))[:keff]
+            assert list(r["sel"][i][h]) == sorted(order), (i, h, r["sel"][i][h], sorted(order))
+
+
+def pin_sequence_invariants(ora):
+    """Over the whole sequence: per kv-head the dK contributions sum to zero
+    (softmax shift invariance, chunk by chunk), and the dV contributions sum to
+    the sum of dO over every chunk's tokens and the head's query group."""
+    s = _seq(k=2, chunks=3, n0=3)
+    x = synth.make_sequence_inputs(s, 43)
+    r = ora.sequence(s, x)
+    G = s.hq // s.hkv
+    for h in range(s.hkv):
+        close(r["dk"][:, h].sum(axis=(0, 1)), np.zeros(s.d), 1e-11, "sum dK")
+        close(r["dv"][:, h].sum(axis=(0, 1)), x["do"][:, :, h * G:(h + 1) * G, :].sum(axis=(0, 1, 2)), 1e-11,
+              "sum dV")
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 

@@ -70,3 +70,14 @@ def test_problem_inputs_layout():
     assert x["k_pool"][pt[n], h, r, xx] == synth.lib().synth_round_bf16(tok + 0.5 * off)
     unmapped = sorted(set(range(9)) - set(pt.tolist()))
     assert all(bf16_value(b) == 64.0 for b in x["k_pool"][unmapped].ravel())
+
+
+def test_sequence_inputs_cover_every_page():
+    s = synth.Sequence(hq=4, hkv=2, d=16, ps=4, c=8, chunks=3, k=2, n0=2)
+    x = synth.make_sequence_inputs(s, 9)
+    assert x["q"].shape == (3, 8, 4, 16) and x["do"].shape == (3, 8, 4, 16)
+    assert x["k_pool"].shape == (s.pages, 2, 4, 16)
+    assert sorted(x["page_table"].tolist()) == list(range(s.pages))
+    assert s.step(0).n == 2 and s.step(2).n == 2 + 2 * 2 and s.step(2).slots == s.pages
+    y = synth.make_sequence_inputs(s, 9)
+    assert all(np.array_equal(x[k], y[k]) for k in x)
