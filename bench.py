@@ -156,6 +156,73 @@ def measured_traffic(kernel, workload):
     return t["traffic_bytes_per_launch"]
 
 
+def sequence_bench(args):
+    """Chunk-recurrent forward (chunks in order) and backward (reverse order) of
+    one layer over a whole synthetic sequence; one JSON line."""
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_sparse_attention_amd as P
+    from paged_sparse_attention_amd.sequence import ChunkedSequence
+
+    seed, s = synth.SEQUENCES[args.sequence]
+    print(f"bench: sequence {args.sequence} {s}", file=sys.stderr, flush=True)
+    x = synth.make_sequence_inputs(s, seed)
+
+    def dev(a, bf=False):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf else t).cuda()
+
+    bf = s.dtype == "bf16"
+    q, k, v, do = dev(x["q"], bf), dev(x["k_pool"], bf), dev(x["v_pool"], bf), dev(x["do"], bf)
+    pt = dev(x["page_table"])
+    del x
+    dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
+                          softmax_scale=s.scale)
+    for _ in range(args.warmup):
+        drv.forward(q, k, v, pt)
+        drv.backward(q, k, v, pt, do, dk, dv)
+    torch.cuda.synchronize()
+    hip = HipEvents(P.hip_runtimes_loaded()[0], 3 * args.steps)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    fwd_ms, bwd_ms = [], []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i]), stream)
+        drv.forward(q, k, v, pt)
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 1]), stream)
+        drv.backward(q, k, v, pt, do, dk, dv)
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 2]), stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        fwd_ms.append(hip.elapsed_ms(3 * i, 3 * i + 1))
+        bwd_ms.append(hip.elapsed_ms(3 * i + 1, 3 * i + 2))
+    ms = (t1 - t0) * 1e3 / args.steps
+    tokens = s.chunks * s.c
+    flops = 14.0 * s.d * s.pairs()
+    peak = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": "chunk-recurrent layer fwd+bwd tokens/s over a whole sequence, Qwen2.5-7B shape",
+        "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "fwd_ms": statistics.mean(fwd_ms),
+        "bwd_ms": statistics.mean(bwd_ms), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": s.dtype, "data": "synthetic",
+        "config": {"workload": args.sequence, "n_q_heads": s.hq, "n_kv_heads": s.hkv, "head_dim": s.d,
+                   "page_size": s.ps, "chunk_len": s.c, "chunks": s.chunks, "tokens": tokens, "top_k": s.k,
+                   "initial_pages": s.n0, "visible_pairs": s.pairs(), "seed": seed},
+        "roofline": {"bound": "mfma", "kernel": "whole pass (every kernel of every chunk)", "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "work_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,11 +231,20 @@ def main():
     ap.add_argument("--workload", default="sparse-256k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=1536, help="chunk tokens in the oracle's timed sample")
+    ap.add_argument("--sequence", default=None, metavar="NAME",
+                    help="instead of one chunk step, time chunk-recurrent forward and backward over a whole "
+                         "sequence (synth.SEQUENCES, e.g. seq-64k)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sequence:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        sequence_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "

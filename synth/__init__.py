@@ -188,6 +188,12 @@ class Sequence:
         return sum(self.step(i).pairs() for i in range(self.chunks))
 
 
+# Whole sequences of the Qwen2.5-7B attention shape, chunk by chunk (name -> (seed, Sequence)).
+SEQUENCES = {
+    "seq-64k": (6, Sequence(hq=28, hkv=4, d=128, ps=128, c=4096, chunks=16, k=64)),
+}
+
+
 def make_sequence_inputs(s: Sequence, seed: int) -> dict:
     """Inputs of a whole sequence: pools and page table of every page, and
     Q / dO of every chunk ([chunks][c][hq][d])."""
