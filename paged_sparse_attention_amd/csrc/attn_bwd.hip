@@ -217,11 +217,19 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   const T* __restrict__ dp = (const T*)a.dout;
   QD qd{lds_q, lds_d};
   const int64_t tok_stride = (int64_t)g.hq * D;
+  const typename QD::Lanes qlanes = QD::lane_offsets(tid, (int)tok_stride);
   auto load = [&](int j) {
     const int gi = tile_head(j), t0 = tile_t0(j);
     const int tmax = g.c - 1 - t0;  // last valid row of the tile
     const int64_t base = ((int64_t)t0 * g.hq + h * g.G + gi) * D;
-    qd.load(j, qp, dp, tid, [=](int r) -> int64_t { return base + (int64_t)min(r, tmax) * tok_stride; });
+    bool done = false;
+    if constexpr (QD::kDirect) {
+      if (tmax >= BM - 1) {  // every row of the tile is a real token
+        qd.load_rows(j, qp, dp, base, qlanes, tid);
+        done = true;
+      }
+    }
+    if (!done) qd.load(j, qp, dp, tid, [=](int r) -> int64_t { return base + (int64_t)min(r, tmax) * tok_stride; });
     if (wave == 0 && lane < BM) {
       const int64_t i = (int64_t)(h * g.G + gi) * g.c + t0 + min(lane, tmax);
       load_lds_dword(a.lse2 + i, rlse[j % QD::NS]);

@@ -244,10 +244,10 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   const T* __restrict__ vp = (const T*)a.v;
   KV kv{lds_k, lds_v};
   const bool tile_in_page = BN <= (1 << g.ps_log2);
+  const typename KV::Lanes lanes = KV::lane_offsets(tid, D);
   auto load = [&](int j) {
     if (tile_in_page) {
-      const int64_t base = pages.key_offset<D>(g, a.pt, a.sel, h, j * BN);
-      kv.load(j, kp, vp, tid, [base](int r) -> int64_t { return base + (int64_t)r * D; });
+      kv.load_rows(j, kp, vp, pages.key_offset<D>(g, a.pt, a.sel, h, j * BN), lanes, tid);
     } else {
       kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t {
         return pages.key_offset<D>(g, a.pt, a.sel, h, min(j * BN + r, nkeys - 1));

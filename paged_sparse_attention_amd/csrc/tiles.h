@@ -168,6 +168,14 @@ __device__ __forceinline__ void wait_vmem_le(int n) {
 //     barrier                                 -- ... and for every wave
 //     load(j + PD) if it exists               -- refills the slot of tile j - 1
 //     read tiles ta(j), tb(j)
+// 1 KB direct-load blocks of a tile (tiles filled through registers have none)
+template <typename TL, bool direct> struct BlockCount {
+  static constexpr int value = 1;
+};
+template <typename TL> struct BlockCount<TL, true> {
+  static constexpr int value = TL::BLOCKS;
+};
+
 template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2> struct Ring {
   typedef Tile<T, D, BR> TL;
   static constexpr bool kDirect = sizeof(T) == 2;
@@ -204,6 +212,48 @@ template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2
     } else {
       sa.load((const float*)srca, tid, off);
       sb.load((const float*)srcb, tid, off);
+    }
+  }
+  // Direct loads of a tile whose rows lie row_stride elements apart (row r at
+  // base + r * row_stride).  The element offsets of a wave's load slots within
+  // a tile never change, so lane_offsets computes them once; a tile then costs
+  // one wave-uniform base per tensor and no per-lane address arithmetic.
+  static constexpr int NW = NT / 64;
+  static constexpr int NBW = (BlockCount<TL, kDirect>::value + NW - 1) / NW;  // 1 KB blocks a wave loads, at most
+  struct Lanes {
+    int off[NBW];
+  };
+  __device__ static __forceinline__ Lanes lane_offsets(int tid, int row_stride) {
+    Lanes l;
+    if constexpr (kDirect) {
+      const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) {
+        const int q = (wave + i * NW) * 64 + lane;
+        const int r = q / TL::SLOTS, p = q % TL::SLOTS;
+        const int c = p < TL::CPR ? (p ^ TL::flip(r)) : 0;
+        l.off[i] = r * row_stride + c * TL::VEC;
+      }
+    }
+    return l;
+  }
+  __device__ __forceinline__ void load_rows(int j, const T* __restrict__ srca, const T* __restrict__ srcb,
+                                            int64_t base, const Lanes& l, int tid) {
+    static_assert(kDirect, "row loads are direct-to-LDS (bf16)");
+    const int wave = tid >> 6;
+    const int64_t b = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((int)base));
+    const T* a0 = srca + b;
+    const T* b0 = srcb + b;
+    T* da = pa + (j % NS) * TL::ELEMS;
+    T* db = pb + (j % NS) * TL::ELEMS;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      const int blk = wave + i * NW;
+      if (blk < TL::BLOCKS) {
+        __builtin_amdgcn_global_load_lds((gbl_void*)(a0 + l.off[i]), (lds_void*)(da + blk * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(b0 + l.off[i]), (lds_void*)(db + blk * 512), 16, 0, 0);
+      }
     }
   }
   // tile j is in LDS as far as this thread is concerned; `newer` tiles were
