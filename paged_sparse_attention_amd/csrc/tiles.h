@@ -159,15 +159,6 @@ __device__ __forceinline__ void wait_vmem_le(int n) {
   }
 }
 
-// Two tensors with the same row addressing (K and V, or Q and dO) streamed
-// through a ring of LDS tile slots.  bf16: three slots and two tiles in flight
-// ahead of the one in use, filled by direct-to-LDS loads; fp32: two slots, one
-// tile in flight staged in registers.  Use, per tile index j:
-//   load(j) for the first PD tiles; then for each j:
-//     commit(j, tiles_issued_after_j, extra) -- tile j has landed for this wave
-//     barrier                                 -- ... and for every wave
-//     load(j + PD) if it exists               -- refills the slot of tile j - 1
-//     read tiles ta(j), tb(j)
 // 1 KB direct-load blocks of a tile (tiles filled through registers have none)
 template <typename TL, bool direct> struct BlockCount {
   static constexpr int value = 1;
@@ -175,6 +166,17 @@ template <typename TL, bool direct> struct BlockCount {
 template <typename TL> struct BlockCount<TL, true> {
   static constexpr int value = TL::BLOCKS;
 };
+
+// Two tensors with the same row addressing (K and V, or Q and dO) streamed
+// through a ring of NSLOTS LDS tile slots, PD = NSLOTS - 1 tiles in flight
+// ahead of the one in use.  bf16 tiles are filled by direct-to-LDS loads (any
+// number of slots); fp32 tiles are staged through registers (two slots, one
+// tile in flight).  Use, per tile index j:
+//   load(j) for the first PD tiles; then for each j:
+//     commit(j, tiles_issued_after_j, extra) -- tile j has landed for this wave
+//     barrier                                 -- ... and for every wave
+//     load(j + PD) if it exists               -- refills the slot of tile j - 1
+//     read tiles ta(j), tb(j)
 
 template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2> struct Ring {
   typedef Tile<T, D, BR> TL;
