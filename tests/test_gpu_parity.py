@@ -33,6 +33,11 @@ SMALL = {
     # are then read from the page table for every tile
     "uncached-pages-dense": (31, Problem(hq=4, hkv=1, d=64, ps=16, c=32, n=1100, k=2000)),
     "uncached-pages-topk": (32, Problem(hq=8, hkv=2, d=128, ps=16, c=64, n=1500, k=1100)),
+    "mha-bf16": (33, Problem(hq=4, hkv=4, d=128, ps=64, c=128, n=10, k=3)),
+    "gqa32-d64": (34, Problem(hq=32, hkv=1, d=64, ps=32, c=64, n=12, k=5)),
+    "ps32-d128": (35, Problem(hq=8, hkv=2, d=128, ps=32, c=96, n=20, k=7)),
+    "k-one-below-n": (36, Problem(hq=4, hkv=2, d=64, ps=16, c=32, n=9, k=8)),
+    "scale-override-bf16": (37, Problem(hq=6, hkv=3, d=128, ps=128, c=128, n=5, k=2, scale=0.2)),
 }
 
 FULL = ["dense-32k", "sparse-256k", "sparse-1m", "sparse-4m"]
