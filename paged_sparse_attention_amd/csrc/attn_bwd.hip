@@ -44,8 +44,8 @@ struct BwdArgs {
   float* dv;
   float* dt;       // workspace [Hq][C]: rowsum(dO * O)
   float* lse2;     // workspace [Hq][C]: lse * log2(e)
-  float* part_k;   // workspace [splits][Hkv][nkeys][D], scaled dK partials
-  float* part_v;   // workspace [splits][Hkv][nkeys][D]
+  float* part_k;   // workspace [splits-1][Hkv][nkeys][D], scaled dK partials of splits 1..
+  float* part_v;   // workspace [splits-1][Hkv][nkeys][D]
   int splits;
   Geo g;
   float scale_log2;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 
   if (!key_ok) return;
   const float sc = g.scale;
-  if (plan.splits == 1) {
+  if (sp == 0) {  // the first split adds straight into the pools; kv_reduce adds the rest after it
     float* dkp = a.dk + koff;
     float* dvp = a.dv + koff;
 #pragma unroll
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
         *reinterpret_cast<f32x4*>(dvp + d) = ov;
       }
   } else {
-    const int64_t base = (((int64_t)sp * g.hkv + h) * nkeys + my_key) * D;
+    const int64_t base = (((int64_t)(sp - 1) * g.hkv + h) * nkeys + my_key) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -347,7 +347,8 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   }
 }
 
-// dk_pool / dv_pool += sum over splits of the partials (fixed order).
+// dk_pool / dv_pool += sum of the partials of splits 1 .. splits-1, in split
+// order (split 0 has already added its share in place).
 template <int D>
 __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
   const Geo& g = a.g;
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
   const int64_t src = hk * D + d;
   f32x4 sk = *reinterpret_cast<const f32x4*>(a.part_k + src);
   f32x4 sv = *reinterpret_cast<const f32x4*>(a.part_v + src);
-  for (int s = 1; s < a.splits; ++s) {
+  for (int s = 1; s < a.splits - 1; ++s) {
     sk += *reinterpret_cast<const f32x4*>(a.part_k + s * stride + src);
     sv += *reinterpret_cast<const f32x4*>(a.part_v + s * stride + src);
   }
@@ -514,7 +515,7 @@ BwdPlan bwd_plan(const Shape& s) {
   size_t off = 2 * rowvec;
   p.splits = kp.splits;
   p.off_part_k = off;
-  const size_t part = kp.splits > 1 ? (size_t)kp.splits * s.hkv * nkeys * s.d * 4 : 0;
+  const size_t part = kp.splits > 1 ? (size_t)(kp.splits - 1) * s.hkv * nkeys * s.d * 4 : 0;
   off += (part + 255) & ~(size_t)255;
   p.off_part_v = off;
   off += (part + 255) & ~(size_t)255;
