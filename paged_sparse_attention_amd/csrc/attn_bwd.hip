@@ -14,9 +14,10 @@
 //      tiles of 32 rows, recomputing S = Q K^T and dP = dO V^T on MFMA, then
 //      dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the
 //      row-major LDS tiles).  When the rows are split over several workgroups
-//      for load balance, each writes its partial sums to the workspace.
+//      for load balance, the first split adds into the pools in place and the
+//      others write partial sums to the workspace.
 //   3. kv_reduce_kernel (only with a row split): dk_pool/dv_pool += the sum of
-//      the partials, in split order.
+//      the other splits' partials, in split order.
 //   4. dq_kernel:   query-major, like the forward: S^T and dP^T per 32-key
 //      block of a K/V tile, dQ^T += K^T dS^T, written once per row.
 // Every (slot, kv-head, row) of the gradient pools is changed by exactly one
