@@ -181,7 +181,7 @@ def sequence_bench(args):
     dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
     drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                          softmax_scale=s.scale)
+                          softmax_scale=s.scale, keep_activations=not args.recompute)
     for _ in range(args.warmup):
         drv.forward(q, k, v, pt)
         drv.backward(q, k, v, pt, do, dk, dv)
@@ -214,7 +214,8 @@ def sequence_bench(args):
         "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": args.sequence, "n_q_heads": s.hq, "n_kv_heads": s.hkv, "head_dim": s.d,
                    "page_size": s.ps, "chunk_len": s.c, "chunks": s.chunks, "tokens": tokens, "top_k": s.k,
-                   "initial_pages": s.n0, "visible_pairs": s.pairs(), "seed": seed},
+                   "initial_pages": s.n0, "visible_pairs": s.pairs(), "seed": seed,
+                   "activations": "one chunk, forward re-run in the backward" if args.recompute else "every chunk kept"},
         "roofline": {"bound": "mfma", "kernel": "whole pass (every kernel of every chunk)", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                      "work_per_launch": flops},
@@ -234,6 +235,9 @@ def main():
     ap.add_argument("--sequence", default=None, metavar="NAME",
                     help="instead of one chunk step, time chunk-recurrent forward and backward over a whole "
                          "sequence (synth.SEQUENCES, e.g. seq-64k)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="with --sequence: keep one chunk's O/LSE and re-run each chunk's forward in the backward "
+                         "(14*D flop per pair are still credited; the re-run forward is extra work)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()

@@ -28,11 +28,13 @@ from .step import TORCH_DTYPE
 
 class ChunkedSequence:
     def __init__(self, n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_chunks, top_k,
-                 n_initial_pages=0, n_slots=None, dtype="bf16", softmax_scale=0.0, device="cuda"):
+                 n_initial_pages=0, n_slots=None, dtype="bf16", softmax_scale=0.0, device="cuda",
+                 keep_activations=True):
         if chunk_len % page_size:
             raise ValueError("chunk_len must be a multiple of page_size")
         self.hq, self.hkv, self.d, self.ps, self.c = n_q_heads, n_kv_heads, head_dim, page_size, chunk_len
         self.n_chunks, self.top_k, self.n0, self.dtype = n_chunks, top_k, n_initial_pages, dtype
+        self.keep_activations = keep_activations
         self.chunk_pages = chunk_len // page_size
         self.total_pages = n_initial_pages + n_chunks * self.chunk_pages
         self.n_slots = self.total_pages if n_slots is None else n_slots
@@ -45,8 +47,9 @@ class ChunkedSequence:
         self.rep = torch.zeros((self.total_pages, n_kv_heads, head_dim), **f32)
         self.sel = [torch.zeros((n_kv_heads, max(self.keff(i), 1)), dtype=torch.int32, device=device)
                     for i in range(n_chunks)]
-        self.o = torch.empty((n_chunks, chunk_len, n_q_heads, head_dim), dtype=TORCH_DTYPE[dtype], device=device)
-        self.lse = torch.empty((n_chunks, n_q_heads, chunk_len), **f32)
+        n_act = n_chunks if keep_activations else 1
+        self.o = torch.empty((n_act, chunk_len, n_q_heads, head_dim), dtype=TORCH_DTYPE[dtype], device=device)
+        self.lse = torch.empty((n_act, n_q_heads, chunk_len), **f32)
         self.dq = torch.empty((n_chunks, chunk_len, n_q_heads, head_dim), **f32)
         ws_sel = max(oomb_select_workspace_bytes(d) for d in self.descs)
         ws_bwd = max(oomb_bwd_workspace_bytes(d) for d in self.descs)
@@ -59,23 +62,37 @@ class ChunkedSequence:
     def keff(self, i):
         return max(0, min(self.top_k, self.prior_pages(i)))
 
-    def forward(self, q, k_pool, v_pool, page_table, stream=None):
+    def _act(self, i):
+        return i if self.keep_activations else 0
+
+    def forward(self, q, k_pool, v_pool, page_table, stream=None, on_chunk=None):
         """Chunks in order: select among the earlier pages, attend, then give the
-        chunk's pages their representative vectors.  Returns (O, LSE)."""
+        chunk's pages their representative vectors.  on_chunk(i, O, LSE), if
+        given, is called after chunk i's forward is enqueued (with one activation
+        buffer, that chunk's O and LSE are overwritten by the next chunk).
+        Returns (O, LSE)."""
         if self.n0 > 0:
             oomb_rep_update(self.descs[0], k_pool, page_table, 0, self.n0, self.rep, stream=stream)
         for i, desc in enumerate(self.descs):
+            a = self._act(i)
             oomb_select_topk(desc, q[i], self.rep, self.sel[i], None, self.ws_select, stream=stream)
-            oomb_attn_fwd(desc, q[i], k_pool, v_pool, page_table, self.sel[i], self.o[i], self.lse[i],
+            oomb_attn_fwd(desc, q[i], k_pool, v_pool, page_table, self.sel[i], self.o[a], self.lse[a],
                           stream=stream)
+            if on_chunk is not None:
+                on_chunk(i, self.o[a], self.lse[a])
             oomb_rep_update(desc, k_pool, page_table, self.prior_pages(i), self.chunk_pages, self.rep,
                             stream=stream)
         return self.o, self.lse
 
     def backward(self, q, k_pool, v_pool, page_table, dO, dk_pool, dv_pool, stream=None):
         """Chunks in reverse order with their forward selections; dK/dV are added
-        into the pools in place.  Returns dQ."""
+        into the pools in place.  Without kept activations each chunk's forward
+        is re-run first, with its saved selection.  Returns dQ."""
         for i in reversed(range(self.n_chunks)):
-            oomb_attn_bwd(self.descs[i], q[i], k_pool, v_pool, page_table, self.sel[i], self.o[i], self.lse[i],
+            a = self._act(i)
+            if not self.keep_activations:
+                oomb_attn_fwd(self.descs[i], q[i], k_pool, v_pool, page_table, self.sel[i], self.o[a],
+                              self.lse[a], stream=stream)
+            oomb_attn_bwd(self.descs[i], q[i], k_pool, v_pool, page_table, self.sel[i], self.o[a], self.lse[a],
                           dO[i], self.dq[i], dk_pool, dv_pool, self.ws_bwd, stream=stream)
         return self.dq
