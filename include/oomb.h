@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define OOMB_ABI_VERSION 1
+#define OOMB_ABI_VERSION 2
 
 typedef enum { OOMB_F32 = 0, OOMB_BF16 = 1 } oomb_dtype;
 
@@ -79,7 +79,8 @@ typedef enum {
   OOMB_ERR_BAD_DTYPE = -4,   /* dtype not an oomb_dtype */
   OOMB_ERR_MISALIGNED = -5,  /* a device pointer is not 16-byte aligned */
   OOMB_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
-  OOMB_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
+  OOMB_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
+  OOMB_ERR_NOT_MAPPED = -8   /* host memory the device cannot address (oomb_host_view) */
 } oomb_status;
 
 /* Host-side descriptor of one chunk step. */
@@ -150,6 +151,69 @@ int oomb_attn_bwd(const oomb_desc* desc, const void* q, const void* k_pool, cons
                   const int32_t* page_table, const int32_t* sel, const void* o, const float* lse,
                   const void* dO, float* dq, float* dk_pool, float* dv_pool, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* ---- CPU offloading of the KV cache and its gradients -------------------
+ * (OOMB, section 2, "Asynchronous CPU Offloading": the KV cache and its
+ * gradients, which grow with the context, live in CPU memory and move to and
+ * from the GPU asynchronously, overlapped with compute.)
+ *
+ * HOST POOLS have the device pools' layout, [n_slots][Hkv][ps][D] (T for K/V,
+ * fp32 for dK/dV), in pinned host memory that the device addresses; the calls
+ * below take the device view of a host buffer (oomb_host_view) where they say
+ * "host pool".  page_table maps logical pages to host-pool slots.
+ *
+ * A chunk step then runs on a device STAGING POOL that holds only what the
+ * step touches: n_stage = Hkv*K_eff + C/ps slots of [Hkv][ps][D],
+ *   slot h*K_eff + k      kv-head h's block of page sel[h][k] (the other heads'
+ *                         blocks of that slot are not used);
+ *   slot Hkv*K_eff + j    every kv-head of the chunk's page N + j.
+ * The four calls above run on it unchanged with the STAGED descriptor
+ * (oomb_stage_desc), the staged selection sel'[h][k] = h*K_eff + k and the
+ * identity page table of length n_stage (oomb_stage_tables).  Every kv-head
+ * then visits the same keys in the same order as on the full pools, so the
+ * forward, dQ and the staged dK/dV blocks are bitwise those of the full-pool
+ * call; gradients go back to the host pools with oomb_stage_flush_grads.
+ *
+ * These calls are asynchronous on `stream` like the others; a copy on one
+ * stream overlaps attention on another (each copy kernel occupies only a few
+ * compute units).  Selection and page-table entries out of range are skipped
+ * (no copy); device pointers must be 16-byte aligned. */
+#define OOMB_STAGE_SELECTED 1 /* the selected (kv-head, page) blocks */
+#define OOMB_STAGE_CHUNK 2    /* every kv-head of the chunk's own pages */
+
+/* Device view of pinned host memory (hipHostMalloc or torch pin_memory), for
+ * the host-pool arguments below (host).  OOMB_ERR_NOT_MAPPED if the device
+ * cannot address host_ptr. */
+int oomb_host_view(const void* host_ptr, void** device_view);
+
+/* Staged descriptor (host, no HIP call): desc with n_prior_pages = Hkv*K_eff,
+ * top_k = K_eff and n_slots = rep_capacity = n_stage. */
+int oomb_stage_desc(const oomb_desc* desc, oomb_desc* staged);
+
+/* sel_stage[i] = i for i < Hkv*K_eff (NULL allowed when K_eff = 0) and
+ * pt_stage[i] = i for i < n_stage (int32, device). */
+int oomb_stage_tables(const oomb_desc* desc, int32_t* sel_stage, int32_t* pt_stage, void* stream);
+
+/* Host pools -> staging pool: the parts (OOMB_STAGE_SELECTED and/or
+ * OOMB_STAGE_CHUNK) of K and V, from host slots page_table[sel[h][k]] and
+ * page_table[N + j]. */
+int oomb_stage_gather(const oomb_desc* desc, const void* host_k, const void* host_v,
+                      const int32_t* page_table, const int32_t* sel, int32_t parts, void* stage_k,
+                      void* stage_v, void* stream);
+
+/* Staging pool -> host pools: every kv-head of the chunk's pages N .. N+C/ps-1
+ * (the chunk's keys and values once it has run), to host slots page_table[N + j]. */
+int oomb_stage_offload_chunk(const oomb_desc* desc, const void* stage_k, const void* stage_v,
+                             const int32_t* page_table, void* host_k, void* host_v, void* stream);
+
+/* Gradient flush (fp32): for the selected blocks and the chunk's pages,
+ * host_dk[block] += stage_dk[block] and host_dv[block] += stage_dv[block], then
+ * those staging blocks are set to zero, ready for the next step's in-place
+ * accumulation.  Flushes that may touch the same host blocks must run in order
+ * (one stream). */
+int oomb_stage_flush_grads(const oomb_desc* desc, float* stage_dk, float* stage_dv,
+                           const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
+                           void* stream);
 
 /* Static text for a status code (host). */
 const char* oomb_status_string(int status);

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "liboomb.so")
 
 OOMB_F32, OOMB_BF16 = 0, 1
 DTYPE_CODES = {"f32": OOMB_F32, "bf16": OOMB_BF16, torch.float32: OOMB_F32, torch.bfloat16: OOMB_BF16}
-ABI_VERSION = 1
+ABI_VERSION = 2
+OOMB_STAGE_SELECTED, OOMB_STAGE_CHUNK = 1, 2
 
 
 class OombError(RuntimeError):
@@ -59,6 +60,12 @@ def _load():
         "oomb_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_bwd_workspace_bytes": (sz, [P]),
         "oomb_attn_bwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "oomb_host_view": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
+        "oomb_stage_desc": (ctypes.c_int, [P, P]),
+        "oomb_stage_tables": (ctypes.c_int, [P, vp, vp, vp]),
+        "oomb_stage_gather": (ctypes.c_int, [P, vp, vp, vp, vp, i32, vp, vp, vp]),
+        "oomb_stage_offload_chunk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
+        "oomb_stage_flush_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "oomb_abi_version": (ctypes.c_int, []),
         "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -147,6 +154,41 @@ def oomb_attn_bwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, dO, dq, dk_p
     _check(_L.oomb_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                             _ptr(sel), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk_pool), _ptr(dv_pool),
                             _ptr(workspace), nbytes, _stream(stream)))
+
+
+def oomb_host_view(host) -> int:
+    """Device address of pinned host memory (a pinned CPU tensor or an int address)."""
+    if isinstance(host, torch.Tensor) and (host.is_cuda or not host.is_pinned()):
+        raise ValueError("oomb_host_view needs a pinned CPU tensor")
+    out = ctypes.c_void_p()
+    _check(_L.oomb_host_view(_ptr(host), ctypes.byref(out)))
+    return out.value
+
+
+def oomb_stage_desc(desc) -> oomb_desc:
+    staged = oomb_desc()
+    _check(_L.oomb_stage_desc(ctypes.byref(desc), ctypes.byref(staged)))
+    return staged
+
+
+def oomb_stage_tables(desc, sel_stage, pt_stage, stream=None):
+    _check(_L.oomb_stage_tables(ctypes.byref(desc), _ptr(sel_stage), _ptr(pt_stage), _stream(stream)))
+
+
+def oomb_stage_gather(desc, host_k, host_v, page_table, sel, parts, stage_k, stage_v, stream=None):
+    """host_k / host_v: device views (oomb_host_view) of the host pools."""
+    _check(_L.oomb_stage_gather(ctypes.byref(desc), _ptr(host_k), _ptr(host_v), _ptr(page_table), _ptr(sel), parts,
+                                _ptr(stage_k), _ptr(stage_v), _stream(stream)))
+
+
+def oomb_stage_offload_chunk(desc, stage_k, stage_v, page_table, host_k, host_v, stream=None):
+    _check(_L.oomb_stage_offload_chunk(ctypes.byref(desc), _ptr(stage_k), _ptr(stage_v), _ptr(page_table),
+                                       _ptr(host_k), _ptr(host_v), _stream(stream)))
+
+
+def oomb_stage_flush_grads(desc, stage_dk, stage_dv, page_table, sel, host_dk, host_dv, stream=None):
+    _check(_L.oomb_stage_flush_grads(ctypes.byref(desc), _ptr(stage_dk), _ptr(stage_dv), _ptr(page_table), _ptr(sel),
+                                     _ptr(host_dk), _ptr(host_dv), _stream(stream)))
 
 
 def oomb_trace_events(events, capacity=None):

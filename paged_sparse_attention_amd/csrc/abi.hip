@@ -148,6 +148,92 @@ OOMB_API int oomb_attn_bwd(const oomb_desc* desc, const void* q, const void* k_p
                                    workspace, (hipStream_t)stream));
 }
 
+OOMB_API int oomb_host_view(const void* host_ptr, void** device_view) {
+  if (!host_ptr || !device_view) return OOMB_ERR_NULL_PTR;
+  void* v = nullptr;
+  if (hipHostGetDevicePointer(&v, const_cast<void*>(host_ptr), 0) != hipSuccess || !v) {
+    (void)hipGetLastError();
+    return OOMB_ERR_NOT_MAPPED;
+  }
+  *device_view = v;
+  return OOMB_OK;
+}
+
+namespace {
+int stage_shape(const oomb_desc* desc, oomb::Shape* s, oomb_desc* staged) {
+  int rc = validate(desc, s);
+  if (rc) return rc;
+  const int nsel = s->hkv * s->keff, n_stage = nsel + s->c / s->ps;
+  *staged = *desc;
+  staged->n_prior_pages = nsel;
+  staged->top_k = s->keff;
+  staged->n_slots = n_stage;
+  staged->rep_capacity = n_stage;
+  return OOMB_OK;
+}
+}  // namespace
+
+OOMB_API int oomb_stage_desc(const oomb_desc* desc, oomb_desc* staged) {
+  if (!staged) return OOMB_ERR_NULL_PTR;
+  oomb::Shape s;
+  oomb_desc t;
+  int rc = stage_shape(desc, &s, &t);
+  if (rc) return rc;
+  oomb::Shape check;
+  if ((rc = validate(&t, &check))) return rc;
+  *staged = t;
+  return OOMB_OK;
+}
+
+OOMB_API int oomb_stage_tables(const oomb_desc* desc, int32_t* sel_stage, int32_t* pt_stage, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({pt_stage}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel_stage}))) return rc;
+  (void)hipGetLastError();
+  return launched(oomb::launch_stage_tables(s, sel_stage, pt_stage, (hipStream_t)stream));
+}
+
+OOMB_API int oomb_stage_gather(const oomb_desc* desc, const void* host_k, const void* host_v,
+                               const int32_t* page_table, const int32_t* sel, int32_t parts, void* stage_k,
+                               void* stage_v, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if (parts < 1 || parts > (OOMB_STAGE_SELECTED | OOMB_STAGE_CHUNK)) return OOMB_ERR_BAD_SHAPE;
+  if ((rc = check_ptrs({host_k, host_v, page_table, stage_k, stage_v}))) return rc;
+  if ((parts & OOMB_STAGE_SELECTED) && s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  const int32_t* sel_used = (parts & OOMB_STAGE_SELECTED) ? sel : nullptr;
+  (void)hipGetLastError();
+  return launched(oomb::launch_stage_copy(s, host_k, host_v, stage_k, stage_v, page_table, sel_used, parts, false,
+                                          (hipStream_t)stream));
+}
+
+OOMB_API int oomb_stage_offload_chunk(const oomb_desc* desc, const void* stage_k, const void* stage_v,
+                                      const int32_t* page_table, void* host_k, void* host_v, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({stage_k, stage_v, page_table, host_k, host_v}))) return rc;
+  (void)hipGetLastError();
+  return launched(oomb::launch_stage_copy(s, host_k, host_v, const_cast<void*>(stage_k), const_cast<void*>(stage_v),
+                                          page_table, nullptr, oomb::kStageChunk, true, (hipStream_t)stream));
+}
+
+OOMB_API int oomb_stage_flush_grads(const oomb_desc* desc, float* stage_dk, float* stage_dv,
+                                    const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
+                                    void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({stage_dk, stage_dv, page_table, host_dk, host_dv}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  (void)hipGetLastError();
+  return launched(
+      oomb::launch_grad_flush(s, stage_dk, stage_dv, host_dk, host_dv, page_table, sel, (hipStream_t)stream));
+}
+
 OOMB_API const char* oomb_status_string(int status) {
   switch (status) {
     case OOMB_OK: return "ok";
@@ -158,6 +244,7 @@ OOMB_API const char* oomb_status_string(int status) {
     case OOMB_ERR_MISALIGNED: return "a device pointer is not 16-byte aligned";
     case OOMB_ERR_WORKSPACE: return "workspace missing or too small";
     case OOMB_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case OOMB_ERR_NOT_MAPPED: return "host memory that the device cannot address";
     default: return "unknown status";
   }
 }

@@ -1,0 +1,193 @@
+// offload.hip -- page-block copies between the host page pools and a device
+// staging pool, for keeping the KV cache and its gradients in CPU memory
+// (OOMB page, technical summary, section 2, "Asynchronous CPU Offloading": the
+// context-length-dependent KV cache and gradients move between GPU and CPU
+// memory asynchronously, overlapped with compute).
+//
+// The host pools are pinned host memory addressed by the device through its
+// mapped view, so one kernel reads or writes them over the host link at full
+// link rate whatever the block size, with the block list taken from the page
+// table and the selection where they already are, on the device.  Separate
+// DMA copies would cost a command each per (page, kv-head) block (32 KB at the
+// Qwen2.5-7B shape), and the DMA engines then run far below link rate.
+//
+// The kernels run on few workgroups (kCopyBlocks), so that on a second stream
+// they take a small share of the compute units from the attention kernels they
+// overlap; each thread keeps four 16-byte accesses in flight, enough to cover
+// the link's latency at that size.
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+#include "trace.h"
+
+namespace oomb {
+
+namespace {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+struct CopyArgs {
+  // tensor t (0: K or dK, 1: V or dV): host pool and staging pool
+  const void* src[2];
+  void* dst[2];
+  const int32_t* pt;   // logical page -> host slot
+  const int32_t* sel;  // [Hkv][K_eff] logical pages
+  int hkv, keff, n, n_host_slots;
+  int first_block, n_blocks;  // block range: [0, hkv*keff) selected, then (C/ps)*hkv chunk blocks
+  int vec_per_block;          // block bytes / 16
+  int to_host;                // 0: host -> staging, 1: staging -> host
+};
+
+// Block b of the staging layout: head h's block of (host slot, staging slot).
+// Returns false for a selection or page-table entry out of range (skipped).
+__device__ inline bool block_place(const CopyArgs& a, int b, int& host_slot, int& stage_slot, int& h) {
+  const int nsel = a.hkv * a.keff;
+  int logical;
+  if (b < nsel) {
+    h = b / a.keff;
+    stage_slot = b;
+    logical = a.sel[b];  // sel[h][k], k = b % keff
+    if (logical < 0 || logical >= a.n) return false;
+  } else {
+    const int j = b - nsel;
+    h = j % a.hkv;
+    stage_slot = nsel + j / a.hkv;
+    logical = a.n + j / a.hkv;
+  }
+  host_slot = a.pt[logical];
+  return host_slot >= 0 && host_slot < a.n_host_slots;
+}
+
+// Plain copies, in either direction.
+__global__ __launch_bounds__(kCopyThreads) void page_copy_kernel(CopyArgs a) {
+  const int items = 2 * a.n_blocks;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it & 1, b = a.first_block + (it >> 1);
+    int hs, ss, h;
+    if (!block_place(a, b, hs, ss, h)) continue;
+    // offsets of the two blocks in 16-byte vectors
+    const int64_t vh = ((int64_t)hs * a.hkv + h) * a.vec_per_block;
+    const int64_t vs = ((int64_t)ss * a.hkv + h) * a.vec_per_block;
+    const int4* __restrict__ s = (const int4*)a.src[t] + (a.to_host ? vs : vh);
+    int4* __restrict__ d = (int4*)a.dst[t] + (a.to_host ? vh : vs);
+    for (int i0 = 0; i0 < a.vec_per_block; i0 += kCopyThreads * kCopyUnroll) {
+      int4 r[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int i = i0 + u * kCopyThreads + threadIdx.x;
+        if (i < a.vec_per_block) r[u] = s[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int i = i0 + u * kCopyThreads + threadIdx.x;
+        if (i < a.vec_per_block) d[i] = r[u];
+      }
+    }
+  }
+}
+
+// Gradient flush: host += staging, then staging = 0 (fp32; src = staging,
+// dst = host pools).
+__global__ __launch_bounds__(kCopyThreads) void grad_flush_kernel(CopyArgs a) {
+  const int items = 2 * a.n_blocks;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it & 1, b = a.first_block + (it >> 1);
+    int hs, ss, h;
+    if (!block_place(a, b, hs, ss, h)) continue;
+    float4* __restrict__ st = (float4*)a.src[t] + ((int64_t)ss * a.hkv + h) * a.vec_per_block;
+    float4* __restrict__ ho = (float4*)a.dst[t] + ((int64_t)hs * a.hkv + h) * a.vec_per_block;
+    for (int i0 = 0; i0 < a.vec_per_block; i0 += kCopyThreads * kCopyUnroll) {
+      float4 x[kCopyUnroll], y[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int i = i0 + u * kCopyThreads + threadIdx.x;
+        if (i < a.vec_per_block) {
+          x[u] = ho[i];
+          y[u] = st[i];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int i = i0 + u * kCopyThreads + threadIdx.x;
+        if (i < a.vec_per_block) {
+          float4 z;
+          z.x = x[u].x + y[u].x;
+          z.y = x[u].y + y[u].y;
+          z.z = x[u].z + y[u].z;
+          z.w = x[u].w + y[u].w;
+          ho[i] = z;
+          st[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+  }
+}
+
+__global__ void stage_tables_kernel(int32_t* sel_stage, int nsel, int32_t* pt_stage, int n_stage) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nsel) sel_stage[i] = i;
+  if (i < n_stage) pt_stage[i] = i;
+}
+
+CopyArgs copy_args(const Shape& s, int eb, const int32_t* pt, const int32_t* sel, int parts) {
+  CopyArgs a{};
+  a.pt = pt;
+  a.sel = sel;
+  a.hkv = s.hkv;
+  a.keff = s.keff;
+  a.n = s.n;
+  a.n_host_slots = s.n_slots;
+  const int nsel = s.hkv * s.keff, nchunk = (s.c / s.ps) * s.hkv;
+  a.first_block = (parts & kStageSelected) ? 0 : nsel;
+  a.n_blocks = ((parts & kStageSelected) ? nsel : 0) + ((parts & kStageChunk) ? nchunk : 0);
+  a.vec_per_block = s.ps * s.d * eb / 16;  // ps * D elements of eb bytes
+  return a;
+}
+
+int copy_grid(const CopyArgs& a) { return std::min(kCopyBlocks, std::max(1, 2 * a.n_blocks)); }
+
+}  // namespace
+
+hipError_t launch_stage_copy(const Shape& s, const void* host_k, const void* host_v, void* stage_k, void* stage_v,
+                             const int32_t* pt, const int32_t* sel, int parts, bool to_host, hipStream_t st) {
+  CopyArgs a = copy_args(s, s.bf16 ? 2 : 4, pt, sel, parts);
+  if (a.n_blocks == 0) return hipSuccess;
+  a.to_host = to_host ? 1 : 0;
+  if (to_host) {
+    a.src[0] = stage_k;
+    a.src[1] = stage_v;
+    a.dst[0] = const_cast<void*>(host_k);
+    a.dst[1] = const_cast<void*>(host_v);
+  } else {
+    a.src[0] = host_k;
+    a.src[1] = host_v;
+    a.dst[0] = stage_k;
+    a.dst[1] = stage_v;
+  }
+  Traced tr(st, to_host ? "page_offload_kernel" : "page_gather_kernel");
+  hipLaunchKernelGGL(page_copy_kernel, dim3(copy_grid(a)), dim3(kCopyThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_flush(const Shape& s, float* stage_dk, float* stage_dv, float* host_dk, float* host_dv,
+                             const int32_t* pt, const int32_t* sel, hipStream_t st) {
+  CopyArgs a = copy_args(s, 4, pt, sel, kStageSelected | kStageChunk);
+  if (a.n_blocks == 0) return hipSuccess;
+  a.src[0] = stage_dk;
+  a.src[1] = stage_dv;
+  a.dst[0] = host_dk;
+  a.dst[1] = host_dv;
+  Traced tr(st, "grad_flush_kernel");
+  hipLaunchKernelGGL(grad_flush_kernel, dim3(copy_grid(a)), dim3(kCopyThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st) {
+  const int nsel = s.hkv * s.keff, n_stage = nsel + s.c / s.ps;
+  hipLaunchKernelGGL(stage_tables_kernel, dim3((n_stage + 255) / 256), dim3(256), 0, st, sel_stage, nsel, pt_stage,
+                     n_stage);
+  return hipGetLastError();
+}
+
+}  // namespace oomb

@@ -1,0 +1,246 @@
+"""Chunk-recurrent attention of one layer with the KV cache and its gradients in
+CPU memory.
+
+The OOMB page's KV-cache stack (technical summary, section 2) adds to paged
+memory and page-level sparse attention an asynchronous CPU offload: the KV
+cache and its gradients, which grow with the context, are kept in CPU memory
+and moved between CPU and GPU asynchronously, overlapped with computation, so
+that the added training time stays small (the page reports under 5%).
+
+This driver runs the same sequence as ChunkedSequence (sequence.py) with the
+K/V pools and the dK/dV pools in pinned host memory.  The GPU holds only, per
+chunk in flight, a staging pool with the blocks that chunk touches (its
+selected (kv-head, page) blocks and its own pages; layout in include/oomb.h),
+plus the representative-vector table, the selections and one chunk's
+activations.  Three streams carry the work:
+
+  compute  chunk pages into staging, rep update, selection, attention
+  h2d      oomb_stage_gather: selected blocks (and, in the backward, the
+           chunk's own pages) from the host pools into a staging buffer
+  d2h      oomb_stage_offload_chunk after a chunk's forward (its keys and
+           values to the host pools) and oomb_stage_flush_grads after its
+           backward (host dK/dV += staged gradients, staging cleared)
+
+Staging is double-buffered, so the copies for one chunk run while the
+neighbouring chunk computes:
+  forward   chunk i+1's selection is made before chunk i's attention (it needs
+            only chunk i's representative vectors), so its gather overlaps
+            chunk i's attention.  This needs every chunk's queries up front,
+            as in this single-layer driver; in a full model the next chunk's
+            queries come from the layer below.
+  backward  chunk i-1's gather and chunk i+1's gradient flush overlap chunk i's
+            backward; flushes run in chunk order on one stream, so the host
+            gradients receive each chunk's contribution in turn.
+
+The attention calls are the library's ordinary entry points on the staging pool
+with the staged descriptor, so every kv-head visits the same keys in the same
+order as on device-resident pools: selections, O, LSE and dQ are bitwise those
+of ChunkedSequence; dK/dV differ only in fp32 rounding (each chunk's
+contribution is summed in staging and then added to the host pool, instead of
+being added to the pool directly).
+
+Marshalling and stream ordering only: every step runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (OOMB_STAGE_CHUNK, OOMB_STAGE_SELECTED, make_desc, oomb_attn_bwd, oomb_attn_fwd,
+               oomb_bwd_workspace_bytes, oomb_host_view, oomb_rep_update, oomb_select_topk,
+               oomb_select_workspace_bytes, oomb_stage_desc, oomb_stage_flush_grads, oomb_stage_gather,
+               oomb_stage_offload_chunk, oomb_stage_tables)
+from .step import TORCH_DTYPE
+
+
+class OffloadedSequence:
+    def __init__(self, n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_chunks, top_k,
+                 n_initial_pages=0, n_slots=None, dtype="bf16", softmax_scale=0.0, device="cuda",
+                 keep_activations=False, n_buffers=2):
+        if chunk_len % page_size:
+            raise ValueError("chunk_len must be a multiple of page_size")
+        if n_buffers < 2:
+            raise ValueError("n_buffers must be at least 2")
+        self.hq, self.hkv, self.d, self.ps, self.c = n_q_heads, n_kv_heads, head_dim, page_size, chunk_len
+        self.n_chunks, self.top_k, self.n0, self.dtype = n_chunks, top_k, n_initial_pages, dtype
+        self.keep_activations, self.nbuf = keep_activations, n_buffers
+        self.chunk_pages = chunk_len // page_size
+        self.total_pages = n_initial_pages + n_chunks * self.chunk_pages
+        self.n_slots = self.total_pages if n_slots is None else n_slots
+        self.descs = [make_desc(n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, self.prior_pages(i), top_k,
+                                self.n_slots, rep_capacity=self.total_pages, dtype=dtype,
+                                softmax_scale=softmax_scale)
+                      for i in range(n_chunks)]
+        self.staged = [oomb_stage_desc(d) for d in self.descs]
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        # staged selection and identity page table, one pair per distinct K_eff
+        self._tables = {}
+        for i, sd in enumerate(self.staged):
+            ke = self.keff(i)
+            if ke not in self._tables:
+                sel_s = torch.zeros(max(self.hkv * ke, 1), **i32)
+                pt_s = torch.zeros(sd.n_slots, **i32)
+                oomb_stage_tables(self.descs[i], sel_s, pt_s)
+                self._tables[ke] = (sel_s, pt_s)
+        # rep update of chunk i's pages reads them from staging: logical page
+        # N_i + j -> staging slot Hkv*K_eff_i + j
+        self._pt_rep = []
+        for i in range(n_chunks):
+            t = torch.zeros(self.prior_pages(i) + self.chunk_pages, **i32)
+            nsel = self.hkv * self.keff(i)
+            t[self.prior_pages(i):] = torch.arange(nsel, nsel + self.chunk_pages, **i32)
+            self._pt_rep.append(t)
+        n_stage = max(sd.n_slots for sd in self.staged)
+        blk = (n_stage, n_kv_heads, page_size, head_dim)
+        self.stage_k = [torch.empty(blk, dtype=TORCH_DTYPE[dtype], device=device) for _ in range(n_buffers)]
+        self.stage_v = [torch.empty(blk, dtype=TORCH_DTYPE[dtype], device=device) for _ in range(n_buffers)]
+        # gradient staging starts at zero; every flush leaves what it read at zero
+        self.stage_dk = [torch.zeros(blk, **f32) for _ in range(n_buffers)]
+        self.stage_dv = [torch.zeros(blk, **f32) for _ in range(n_buffers)]
+        self.rep = torch.zeros((self.total_pages, n_kv_heads, head_dim), **f32)
+        self.sel = [torch.zeros((n_kv_heads, max(self.keff(i), 1)), **i32) for i in range(n_chunks)]
+        n_act = n_chunks if keep_activations else 1
+        self.o = torch.empty((n_act, chunk_len, n_q_heads, head_dim), dtype=TORCH_DTYPE[dtype], device=device)
+        self.lse = torch.empty((n_act, n_q_heads, chunk_len), **f32)
+        self.dq = torch.empty((n_chunks, chunk_len, n_q_heads, head_dim), **f32)
+        ws_sel = max(oomb_select_workspace_bytes(d) for d in self.descs)
+        ws_bwd = max(oomb_bwd_workspace_bytes(d) for d in self.staged)
+        self.ws_select = torch.empty(max(ws_sel, 256), dtype=torch.uint8, device=device)
+        self.ws_bwd = torch.empty(max(ws_bwd, 256), dtype=torch.uint8, device=device)
+        self.h2d = torch.cuda.Stream(device=device)
+        self.d2h = torch.cuda.Stream(device=device)
+
+    def prior_pages(self, i):
+        return self.n0 + i * self.chunk_pages
+
+    def keff(self, i):
+        return max(0, min(self.top_k, self.prior_pages(i)))
+
+    def _act(self, i):
+        return i if self.keep_activations else 0
+
+    def _staged_call_args(self, i, b):
+        sel_s, pt_s = self._tables[self.keff(i)]
+        return self.staged[i], sel_s, pt_s, self.stage_k[b], self.stage_v[b]
+
+    @staticmethod
+    def _views(*host):
+        return [oomb_host_view(h) for h in host]
+
+    def forward(self, q, k_new, v_new, host_k, host_v, page_table, on_chunk=None):
+        """q [chunks][C][Hq][D] and the chunks' own keys/values k_new, v_new
+        [chunks][C/ps][Hkv][ps][D] on the device; host_k, host_v: pinned host
+        pools [n_slots][Hkv][ps][D] holding the initial context (the chunks'
+        pages are written into them here); page_table: int32 [total pages] on
+        the device, logical page -> host slot.  on_chunk(i, O, LSE) as in
+        ChunkedSequence.  Runs on the current stream; returns (O, LSE)."""
+        hk, hv = self._views(host_k, host_v)
+        comp = torch.cuda.current_stream()
+        ev = lambda: torch.cuda.Event()
+        fwd_done = [None] * self.n_chunks
+        offloaded = [None] * self.n_chunks
+        gathered = [None] * self.n_chunks
+
+        def gather_selected(i):
+            b = i % self.nbuf
+            ready = ev()
+            ready.record(comp)  # selection of chunk i made
+            with torch.cuda.stream(self.h2d):
+                self.h2d.wait_event(ready)
+                if i >= 1 and offloaded[i - 1] is not None:
+                    self.h2d.wait_event(offloaded[i - 1])  # chunk i-1's pages are in the host pools
+                if i >= self.nbuf:  # buffer b's previous chunk has run and been offloaded
+                    self.h2d.wait_event(fwd_done[i - self.nbuf])
+                    self.h2d.wait_event(offloaded[i - self.nbuf])
+                if self.keff(i) > 0:
+                    oomb_stage_gather(self.descs[i], hk, hv, page_table, self.sel[i], OOMB_STAGE_SELECTED,
+                                      self.stage_k[b], self.stage_v[b], stream=self.h2d)
+                gathered[i] = ev()
+                gathered[i].record(self.h2d)
+
+        if self.n0 > 0:  # representative vectors of the initial context, read through the host view
+            oomb_rep_update(self.descs[0], hk, page_table, 0, self.n0, self.rep)
+        if self.keff(0) > 0:
+            oomb_select_topk(self.descs[0], q[0], self.rep, self.sel[0], None, self.ws_select)
+        gather_selected(0)
+        for i in range(self.n_chunks):
+            b, a = i % self.nbuf, self._act(i)
+            sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
+            nsel = self.hkv * self.keff(i)
+            if i >= self.nbuf:
+                comp.wait_event(offloaded[i - self.nbuf])  # buffer b's chunk pages are in the host pools
+            sk[nsel:nsel + self.chunk_pages].copy_(k_new[i])
+            sv[nsel:nsel + self.chunk_pages].copy_(v_new[i])
+            oomb_rep_update(self.descs[i], sk, self._pt_rep[i], self.prior_pages(i), self.chunk_pages, self.rep)
+            local = ev()
+            local.record(comp)
+            with torch.cuda.stream(self.d2h):
+                self.d2h.wait_event(local)
+                oomb_stage_offload_chunk(self.descs[i], sk, sv, page_table, hk, hv, stream=self.d2h)
+                offloaded[i] = ev()
+                offloaded[i].record(self.d2h)
+            if i + 1 < self.n_chunks:
+                if self.keff(i + 1) > 0:
+                    oomb_select_topk(self.descs[i + 1], q[i + 1], self.rep, self.sel[i + 1], None, self.ws_select)
+                gather_selected(i + 1)
+            comp.wait_event(gathered[i])
+            oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a])
+            fwd_done[i] = ev()
+            fwd_done[i].record(comp)
+            if on_chunk is not None:
+                on_chunk(i, self.o[a], self.lse[a])
+        comp.wait_event(offloaded[-1])
+        return self.o, self.lse
+
+    def backward(self, q, dO, host_k, host_v, host_dk, host_dv, page_table):
+        """Chunks in reverse order with their forward selections; host_dk and
+        host_dv (pinned fp32 pools) receive the gradients in place.  The forward
+        must have run (it wrote the chunks' pages into host_k / host_v); without
+        kept activations each chunk's forward is re-run on its staged blocks.
+        Runs on the current stream; when it completes, host_dk / host_dv are
+        final.  Returns dQ."""
+        hk, hv, hdk, hdv = self._views(host_k, host_v, host_dk, host_dv)
+        comp = torch.cuda.current_stream()
+        ev = lambda: torch.cuda.Event()
+        start = ev()
+        start.record(comp)  # after the forward, including its last offload
+        bwd_done = [None] * self.n_chunks
+        flushed = [None] * self.n_chunks
+        gathered = [None] * self.n_chunks
+
+        def gather(i):
+            b = i % self.nbuf
+            with torch.cuda.stream(self.h2d):
+                self.h2d.wait_event(start)
+                if i + self.nbuf < self.n_chunks:  # buffer b's previous chunk has run
+                    self.h2d.wait_event(bwd_done[i + self.nbuf])
+                oomb_stage_gather(self.descs[i], hk, hv, page_table, self.sel[i],
+                                  OOMB_STAGE_SELECTED | OOMB_STAGE_CHUNK, self.stage_k[b], self.stage_v[b],
+                                  stream=self.h2d)
+                gathered[i] = ev()
+                gathered[i].record(self.h2d)
+
+        last = self.n_chunks - 1
+        gather(last)
+        for i in reversed(range(self.n_chunks)):
+            b, a = i % self.nbuf, self._act(i)
+            sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
+            comp.wait_event(gathered[i])
+            if i + self.nbuf <= last:
+                comp.wait_event(flushed[i + self.nbuf])  # gradient staging b is back at zero
+            if not self.keep_activations:
+                oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a])
+            oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
+                          self.stage_dk[b], self.stage_dv[b], self.ws_bwd)
+            bwd_done[i] = ev()
+            bwd_done[i].record(comp)
+            if i > 0:
+                gather(i - 1)
+            with torch.cuda.stream(self.d2h):
+                self.d2h.wait_event(bwd_done[i])
+                oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table, self.sel[i],
+                                       hdk, hdv, stream=self.d2h)
+                flushed[i] = ev()
+                flushed[i].record(self.d2h)
+        comp.wait_event(flushed[0])
+        return self.dq

@@ -13,7 +13,7 @@ import paged_sparse_attention_amd as P
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "oomb.h")
 
-OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH, NOT_MAPPED = 0, -1, -2, -3, -4, -5, -6, -7, -8
 A = 0x10000        # a fake, 16-byte aligned device address
 B = 0x20000
 
@@ -37,8 +37,8 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert P.oomb_abi_version() == P.ABI_VERSION == 1
-    for code in (OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH):
+    assert P.oomb_abi_version() == P.ABI_VERSION == 2
+    for code in (OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH, NOT_MAPPED):
         assert P.oomb_status_string(code) and P.oomb_status_string(code) != "unknown status"
     assert P.oomb_status_string(-99) == "unknown status"
 
@@ -136,3 +136,39 @@ def test_binding_raises():
     with pytest.raises(P.OombError) as e:
         P.oomb_attn_fwd(good(head_dim=80), A, A, A, A, A, A, A, stream=0)
     assert e.value.status == UNSUPPORTED
+
+
+# ---- offload entry points: the staged descriptor (host arithmetic only) and
+# argument checks that fail before any HIP call
+
+def test_stage_desc():
+    d = good()                                    # Hkv 4, K 64 of N 2048, C/ps 32
+    s = P.oomb_stage_desc(d)
+    assert (s.n_prior_pages, s.top_k, s.n_slots, s.rep_capacity) == (256, 64, 288, 288)
+    assert (s.n_q_heads, s.n_kv_heads, s.head_dim, s.page_size, s.chunk_len, s.dtype) == (28, 4, 128, 128, 4096, 1)
+    s = P.oomb_stage_desc(good(n_prior_pages=10, top_k=64, n_slots=42))   # K_eff = N = 10
+    assert (s.n_prior_pages, s.top_k, s.n_slots) == (40, 10, 72)
+    s = P.oomb_stage_desc(good(n_prior_pages=0, n_slots=32))              # first chunk: no prior pages
+    assert (s.n_prior_pages, s.top_k, s.n_slots) == (0, 0, 32)
+    with pytest.raises(P.OombError) as e:
+        P.oomb_stage_desc(good(chunk_len=4000))
+    assert e.value.status == BAD_SHAPE
+    assert P._L.oomb_stage_desc(P.ctypes.byref(good()), None) == NULL_PTR
+
+
+def test_stage_calls_reject_bad_arguments():
+    d = P.ctypes.byref(good())
+    L = P._L
+    assert L.oomb_stage_gather(d, A, A, A, A, 0, A, A, None) == BAD_SHAPE          # no part
+    assert L.oomb_stage_gather(d, A, A, A, A, 4, A, A, None) == BAD_SHAPE          # unknown part
+    assert L.oomb_stage_gather(d, None, A, A, A, 3, A, A, None) == NULL_PTR
+    assert L.oomb_stage_gather(d, A, A, A, None, 1, A, A, None) == NULL_PTR        # selection needed
+    assert L.oomb_stage_gather(d, A + 4, A, A, A, 3, A, A, None) == MISALIGNED
+    assert L.oomb_stage_offload_chunk(d, A, A, A, None, A, None) == NULL_PTR
+    assert L.oomb_stage_flush_grads(d, A, A, A, None, A, A, None) == NULL_PTR
+    assert L.oomb_stage_flush_grads(d, A, A, A, A, A, A + 8, None) == MISALIGNED
+    assert L.oomb_stage_tables(d, A, None, None) == NULL_PTR
+    assert L.oomb_stage_tables(P.ctypes.byref(good(head_dim=96)), A, A, None) == UNSUPPORTED
+    out = P.ctypes.c_void_p()
+    assert L.oomb_host_view(None, P.ctypes.byref(out)) == NULL_PTR
+    assert L.oomb_host_view(A, None) == NULL_PTR
