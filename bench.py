@@ -156,9 +156,35 @@ def measured_traffic(kernel, workload):
     return t["traffic_bytes_per_launch"]
 
 
+def _time_passes(args, fwd, bwd, hip_path):
+    """W untimed, then K timed forward+backward passes on the current stream.
+    Returns (ms per pass by the host clock, forward ms, backward ms by events)."""
+    import torch
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    hip = HipEvents(hip_path, 3 * args.steps)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i]), stream)
+        fwd()
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 1]), stream)
+        bwd()
+        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 2]), stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    f = statistics.mean(hip.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps))
+    b = statistics.mean(hip.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps))
+    return (t1 - t0) * 1e3 / args.steps, f, b
+
+
 def sequence_bench(args):
     """Chunk-recurrent forward (chunks in order) and backward (reverse order) of
-    one layer over a whole synthetic sequence; one JSON line."""
+    one layer over a whole synthetic sequence; one JSON line.  With --offload
+    the K/V and dK/dV pools live in pinned host memory (OffloadedSequence) and
+    the resident driver is timed in the same process for the overhead."""
     import numpy as np
     import torch
 
@@ -177,31 +203,49 @@ def sequence_bench(args):
     bf = s.dtype == "bf16"
     q, k, v, do = dev(x["q"], bf), dev(x["k_pool"], bf), dev(x["v_pool"], bf), dev(x["do"], bf)
     pt = dev(x["page_table"])
-    del x
     dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    keep = not args.recompute
     drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                          softmax_scale=s.scale, keep_activations=not args.recompute)
-    for _ in range(args.warmup):
-        drv.forward(q, k, v, pt)
-        drv.backward(q, k, v, pt, do, dk, dv)
-    torch.cuda.synchronize()
-    hip = HipEvents(P.hip_runtimes_loaded()[0], 3 * args.steps)
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    fwd_ms, bwd_ms = [], []
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i]), stream)
-        drv.forward(q, k, v, pt)
-        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 1]), stream)
-        drv.backward(q, k, v, pt, do, dk, dv)
-        hip.rt.hipEventRecord(ctypes.c_void_p(hip.handles[3 * i + 2]), stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        fwd_ms.append(hip.elapsed_ms(3 * i, 3 * i + 1))
-        bwd_ms.append(hip.elapsed_ms(3 * i + 1, 3 * i + 2))
-    ms = (t1 - t0) * 1e3 / args.steps
+                          softmax_scale=s.scale, keep_activations=keep)
+    hip_path = P.hip_runtimes_loaded()[0]
+    ms, fwd_ms, bwd_ms = _time_passes(args, lambda: drv.forward(q, k, v, pt),
+                                      lambda: drv.backward(q, k, v, pt, do, dk, dv), hip_path)
+    resident = {"ms_per_step": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms}
+    offload = None
+    if args.offload:
+        from paged_sparse_attention_amd.offload import OffloadedSequence
+        pinned = lambda a, bf16: (torch.from_numpy(np.ascontiguousarray(a)).view(torch.bfloat16) if bf16
+                                  else torch.from_numpy(np.ascontiguousarray(a))).pin_memory()
+        host_k, host_v = pinned(x["k_pool"], bf), pinned(x["v_pool"], bf)
+        host_dk = torch.zeros(k.shape, dtype=torch.float32).pin_memory()
+        host_dv = torch.zeros(k.shape, dtype=torch.float32).pin_memory()
+        # each chunk's own pages, as the layer's K/V projection would hand them over
+        idx = torch.arange(s.chunk_pages, device="cuda")
+        slots = torch.stack([pt[s.n0 + i * s.chunk_pages + idx].long() for i in range(s.chunks)])
+        k_new, v_new = k[slots], v[slots]
+        del k, v, dk, dv, drv
+        torch.cuda.empty_cache()
+        off = OffloadedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
+                                softmax_scale=s.scale, keep_activations=keep, copy_cus=args.copy_cus)
+        ms, fwd_ms, bwd_ms = _time_passes(
+            args, lambda: off.forward(q, k_new, v_new, host_k, host_v, pt),
+            lambda: off.backward(q, do, host_k, host_v, host_dk, host_dv, pt), hip_path)
+        eb, blk = (2 if bf else 4), s.ps * s.d
+        h2d = d2h = 0
+        for i in range(s.chunks):
+            ke, cp = off.keff(i), s.chunk_pages * s.hkv
+            h2d += 2 * s.hkv * ke * blk * eb                          # forward: selected K/V blocks
+            d2h += 2 * cp * blk * eb                                  # forward: the chunk's K/V pages
+            h2d += 2 * (s.hkv * ke + cp) * blk * eb                   # backward: selected and chunk K/V
+            h2d += 2 * (s.hkv * ke + cp) * blk * 4                    # backward: host dK/dV read ...
+            d2h += 2 * (s.hkv * ke + cp) * blk * 4                    # ... and written back
+        offload = {"overhead_vs_resident": ms / resident["ms_per_step"] - 1.0, "copy_cus": args.copy_cus,
+                   "host_to_device_bytes_per_step": h2d, "device_to_host_bytes_per_step": d2h,
+                   "host_pool_bytes": 2 * host_k.numel() * eb + 2 * host_dk.numel() * 4,
+                   "device_staging_bytes": sum(t.numel() * t.element_size()
+                                               for t in off.stage_k + off.stage_v + off.stage_dk + off.stage_dv)}
+    del x
     tokens = s.chunks * s.c
     flops = 14.0 * s.d * s.pairs()
     peak = PEAK_BF16_TFLOPS if s.dtype == "bf16" else PEAK_FP32_TFLOPS
@@ -209,18 +253,21 @@ def sequence_bench(args):
     out = {
         "metric": "chunk-recurrent layer fwd+bwd tokens/s over a whole sequence, Qwen2.5-7B shape",
         "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "fwd_ms": statistics.mean(fwd_ms),
-        "bwd_ms": statistics.mean(bwd_ms), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": s.dtype, "data": "synthetic",
+        "warmup": args.warmup, "ms_per_step": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype, "data": "synthetic",
         "config": {"workload": args.sequence, "n_q_heads": s.hq, "n_kv_heads": s.hkv, "head_dim": s.d,
                    "page_size": s.ps, "chunk_len": s.c, "chunks": s.chunks, "tokens": tokens, "top_k": s.k,
                    "initial_pages": s.n0, "visible_pairs": s.pairs(), "seed": seed,
-                   "activations": "one chunk, forward re-run in the backward" if args.recompute else "every chunk kept"},
+                   "activations": "one chunk, forward re-run in the backward" if args.recompute else "every chunk kept",
+                   "kv_cache": "pinned host memory, staged per chunk" if args.offload else "device"},
         "roofline": {"bound": "mfma", "kernel": "whole pass (every kernel of every chunk)", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
                      "work_per_launch": flops},
         "cpu_baseline": None,
     }
+    if offload is not None:
+        out["resident"] = resident
+        out["offload"] = offload
     print(json.dumps(out), flush=True)
 
 
@@ -238,6 +285,11 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="with --sequence: keep one chunk's O/LSE and re-run each chunk's forward in the backward "
                          "(14*D flop per pair are still credited; the re-run forward is extra work)")
+    ap.add_argument("--offload", action="store_true",
+                    help="with --sequence: K/V and dK/dV pools in pinned host memory (OffloadedSequence); the "
+                         "resident driver is timed too, for the overhead")
+    ap.add_argument("--copy-cus", type=int, default=0,
+                    help="with --offload: compute units reserved for the copy kernels (0: no partition)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()

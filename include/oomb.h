@@ -194,12 +194,16 @@ int oomb_stage_desc(const oomb_desc* desc, oomb_desc* staged);
  * pt_stage[i] = i for i < n_stage (int32, device). */
 int oomb_stage_tables(const oomb_desc* desc, int32_t* sel_stage, int32_t* pt_stage, void* stream);
 
-/* Host pools -> staging pool: the parts (OOMB_STAGE_SELECTED and/or
- * OOMB_STAGE_CHUNK) of K and V, from host slots page_table[sel[h][k]] and
- * page_table[N + j]. */
-int oomb_stage_gather(const oomb_desc* desc, const void* host_k, const void* host_v,
-                      const int32_t* page_table, const int32_t* sel, int32_t parts, void* stage_k,
-                      void* stage_v, void* stream);
+/* Pools -> staging pool: the parts (OOMB_STAGE_SELECTED and/or
+ * OOMB_STAGE_CHUNK) of K and V, from slots page_table[sel[h][k]] and
+ * page_table[N + j] of the source pools src_k / src_v ([src_slots][Hkv][ps][D];
+ * the device view of the host pools, or device pools such as another staging
+ * pool).  Selected blocks are copied only for logical pages in
+ * [first_page, first_page + n_pages); pass 0 and N for all of them.  Entries
+ * that map outside the src_slots slots are skipped. */
+int oomb_stage_gather(const oomb_desc* desc, const void* src_k, const void* src_v, int32_t src_slots,
+                      const int32_t* page_table, const int32_t* sel, int32_t parts, int32_t first_page,
+                      int32_t n_pages, void* stage_k, void* stage_v, void* stream);
 
 /* Staging pool -> host pools: every kv-head of the chunk's pages N .. N+C/ps-1
  * (the chunk's keys and values once it has run), to host slots page_table[N + j]. */

@@ -63,7 +63,7 @@ def _load():
         "oomb_host_view": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "oomb_stage_desc": (ctypes.c_int, [P, P]),
         "oomb_stage_tables": (ctypes.c_int, [P, vp, vp, vp]),
-        "oomb_stage_gather": (ctypes.c_int, [P, vp, vp, vp, vp, i32, vp, vp, vp]),
+        "oomb_stage_gather": (ctypes.c_int, [P, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "oomb_stage_offload_chunk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "oomb_stage_flush_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -175,10 +175,15 @@ def oomb_stage_tables(desc, sel_stage, pt_stage, stream=None):
     _check(_L.oomb_stage_tables(ctypes.byref(desc), _ptr(sel_stage), _ptr(pt_stage), _stream(stream)))
 
 
-def oomb_stage_gather(desc, host_k, host_v, page_table, sel, parts, stage_k, stage_v, stream=None):
-    """host_k / host_v: device views (oomb_host_view) of the host pools."""
-    _check(_L.oomb_stage_gather(ctypes.byref(desc), _ptr(host_k), _ptr(host_v), _ptr(page_table), _ptr(sel), parts,
-                                _ptr(stage_k), _ptr(stage_v), _stream(stream)))
+def oomb_stage_gather(desc, src_k, src_v, page_table, sel, parts, stage_k, stage_v, src_slots=None, first_page=0,
+                      n_pages=None, stream=None):
+    """src_k / src_v: device views (oomb_host_view) of the host pools, or device
+    pools; src_slots defaults to the descriptor's n_slots, the page range to
+    every prior page."""
+    _check(_L.oomb_stage_gather(ctypes.byref(desc), _ptr(src_k), _ptr(src_v),
+                                desc.n_slots if src_slots is None else src_slots, _ptr(page_table), _ptr(sel), parts,
+                                first_page, desc.n_prior_pages if n_pages is None else n_pages, _ptr(stage_k),
+                                _ptr(stage_v), _stream(stream)))
 
 
 def oomb_stage_offload_chunk(desc, stage_k, stage_v, page_table, host_k, host_v, stream=None):

@@ -3,6 +3,8 @@
 // enqueue the kernels on the caller's stream.  Nothing is allocated, freed or
 // synchronised here.
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "launch.h"
@@ -195,19 +197,21 @@ OOMB_API int oomb_stage_tables(const oomb_desc* desc, int32_t* sel_stage, int32_
   return launched(oomb::launch_stage_tables(s, sel_stage, pt_stage, (hipStream_t)stream));
 }
 
-OOMB_API int oomb_stage_gather(const oomb_desc* desc, const void* host_k, const void* host_v,
-                               const int32_t* page_table, const int32_t* sel, int32_t parts, void* stage_k,
-                               void* stage_v, void* stream) {
+OOMB_API int oomb_stage_gather(const oomb_desc* desc, const void* src_k, const void* src_v, int32_t src_slots,
+                               const int32_t* page_table, const int32_t* sel, int32_t parts, int32_t first_page,
+                               int32_t n_pages, void* stage_k, void* stage_v, void* stream) {
   oomb::Shape s;
   int rc = validate(desc, &s);
   if (rc) return rc;
   if (parts < 1 || parts > (OOMB_STAGE_SELECTED | OOMB_STAGE_CHUNK)) return OOMB_ERR_BAD_SHAPE;
-  if ((rc = check_ptrs({host_k, host_v, page_table, stage_k, stage_v}))) return rc;
+  if (src_slots <= 0 || first_page < 0 || n_pages < 0) return OOMB_ERR_BAD_SHAPE;
+  if ((rc = check_ptrs({src_k, src_v, page_table, stage_k, stage_v}))) return rc;
   if ((parts & OOMB_STAGE_SELECTED) && s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
   const int32_t* sel_used = (parts & OOMB_STAGE_SELECTED) ? sel : nullptr;
+  const int64_t hi = std::min<int64_t>((int64_t)first_page + n_pages, s.n);
   (void)hipGetLastError();
-  return launched(oomb::launch_stage_copy(s, host_k, host_v, stage_k, stage_v, page_table, sel_used, parts, false,
-                                          (hipStream_t)stream));
+  return launched(oomb::launch_stage_copy(s, src_k, src_v, stage_k, stage_v, page_table, sel_used, parts, false,
+                                          src_slots, first_page, (int)hi, (hipStream_t)stream));
 }
 
 OOMB_API int oomb_stage_offload_chunk(const oomb_desc* desc, const void* stage_k, const void* stage_v,
@@ -218,7 +222,8 @@ OOMB_API int oomb_stage_offload_chunk(const oomb_desc* desc, const void* stage_k
   if ((rc = check_ptrs({stage_k, stage_v, page_table, host_k, host_v}))) return rc;
   (void)hipGetLastError();
   return launched(oomb::launch_stage_copy(s, host_k, host_v, const_cast<void*>(stage_k), const_cast<void*>(stage_v),
-                                          page_table, nullptr, oomb::kStageChunk, true, (hipStream_t)stream));
+                                          page_table, nullptr, oomb::kStageChunk, true, s.n_slots, 0, s.n,
+                                          (hipStream_t)stream));
 }
 
 OOMB_API int oomb_stage_flush_grads(const oomb_desc* desc, float* stage_dk, float* stage_dv,

@@ -62,9 +62,12 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const v
 // Page-block copies between host page pools and a device staging pool.
 constexpr int kStageSelected = 1;  // the selected (kv-head, page) blocks
 constexpr int kStageChunk = 2;     // every kv-head of the chunk's own pages
-constexpr int kCopyBlocks = 16;    // workgroups of one copy kernel
+constexpr int kCopyBlocks = 8;     // workgroups of one copy kernel
+// host_k / host_v: the pools on the host side of the copy (src_slots slots);
+// selected blocks are copied only for logical pages in [page_lo, page_hi).
 hipError_t launch_stage_copy(const Shape& s, const void* host_k, const void* host_v, void* stage_k, void* stage_v,
-                             const int32_t* pt, const int32_t* sel, int parts, bool to_host, hipStream_t st);
+                             const int32_t* pt, const int32_t* sel, int parts, bool to_host, int src_slots,
+                             int page_lo, int page_hi, hipStream_t st);
 hipError_t launch_grad_flush(const Shape& s, float* stage_dk, float* stage_dv, float* host_dk, float* host_dv,
                              const int32_t* pt, const int32_t* sel, hipStream_t st);
 hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st);

@@ -11,10 +11,13 @@
 // DMA copies would cost a command each per (page, kv-head) block (32 KB at the
 // Qwen2.5-7B shape), and the DMA engines then run far below link rate.
 //
-// The kernels run on few workgroups (kCopyBlocks), so that on a second stream
-// they take a small share of the compute units from the attention kernels they
-// overlap; each thread keeps four 16-byte accesses in flight, enough to cover
-// the link's latency at that size.
+// The kernels run on few workgroups (kCopyBlocks of kCopyThreads), so that on
+// a second stream they take a small share of the compute units from the
+// attention kernels they overlap (a compute unit that holds a copy wave has no
+// room left for an attention workgroup, whose waves fill its register files);
+// each thread keeps four 16-byte accesses in flight.  Fewer, larger copy
+// workgroups were slower: the link rate a compute unit sustains is limited by
+// its own outstanding requests.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -24,8 +27,8 @@ namespace oomb {
 
 namespace {
 
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyThreads = 512;
+constexpr int kCopyUnroll = 4;  // 16-byte accesses in flight per thread
 
 struct CopyArgs {
   // tensor t (0: K or dK, 1: V or dV): host pool and staging pool
@@ -34,6 +37,7 @@ struct CopyArgs {
   const int32_t* pt;   // logical page -> host slot
   const int32_t* sel;  // [Hkv][K_eff] logical pages
   int hkv, keff, n, n_host_slots;
+  int page_lo, page_hi;       // selected blocks of logical pages outside [page_lo, page_hi) are skipped
   int first_block, n_blocks;  // block range: [0, hkv*keff) selected, then (C/ps)*hkv chunk blocks
   int vec_per_block;          // block bytes / 16
   int to_host;                // 0: host -> staging, 1: staging -> host
@@ -48,7 +52,7 @@ __device__ inline bool block_place(const CopyArgs& a, int b, int& host_slot, int
     h = b / a.keff;
     stage_slot = b;
     logical = a.sel[b];  // sel[h][k], k = b % keff
-    if (logical < 0 || logical >= a.n) return false;
+    if (logical < 0 || logical >= a.n || logical < a.page_lo || logical >= a.page_hi) return false;
   } else {
     const int j = b - nsel;
     h = j % a.hkv;
@@ -71,18 +75,20 @@ __global__ __launch_bounds__(kCopyThreads) void page_copy_kernel(CopyArgs a) {
     const int64_t vs = ((int64_t)ss * a.hkv + h) * a.vec_per_block;
     const int4* __restrict__ s = (const int4*)a.src[t] + (a.to_host ? vs : vh);
     int4* __restrict__ d = (int4*)a.dst[t] + (a.to_host ? vh : vs);
-    for (int i0 = 0; i0 < a.vec_per_block; i0 += kCopyThreads * kCopyUnroll) {
-      int4 r[kCopyUnroll];
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int i = i0 + u * kCopyThreads + threadIdx.x;
-        if (i < a.vec_per_block) r[u] = s[i];
-      }
-#pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int i = i0 + u * kCopyThreads + threadIdx.x;
-        if (i < a.vec_per_block) d[i] = r[u];
-      }
+    // four loads in flight per thread, held in named registers: a private
+    // array here is placed in LDS by the compiler, and 16 KB of LDS would keep
+    // this kernel off the compute units an attention kernel occupies
+    const int n = a.vec_per_block;
+    for (int i = threadIdx.x; i < n; i += kCopyThreads * kCopyUnroll) {
+      int4 r0, r1, r2, r3;
+      r0 = s[i];
+      if (i + kCopyThreads < n) r1 = s[i + kCopyThreads];
+      if (i + 2 * kCopyThreads < n) r2 = s[i + 2 * kCopyThreads];
+      if (i + 3 * kCopyThreads < n) r3 = s[i + 3 * kCopyThreads];
+      d[i] = r0;
+      if (i + kCopyThreads < n) d[i + kCopyThreads] = r1;
+      if (i + 2 * kCopyThreads < n) d[i + 2 * kCopyThreads] = r2;
+      if (i + 3 * kCopyThreads < n) d[i + 3 * kCopyThreads] = r3;
     }
   }
 }
@@ -138,6 +144,8 @@ CopyArgs copy_args(const Shape& s, int eb, const int32_t* pt, const int32_t* sel
   a.keff = s.keff;
   a.n = s.n;
   a.n_host_slots = s.n_slots;
+  a.page_lo = 0;
+  a.page_hi = s.n;
   const int nsel = s.hkv * s.keff, nchunk = (s.c / s.ps) * s.hkv;
   a.first_block = (parts & kStageSelected) ? 0 : nsel;
   a.n_blocks = ((parts & kStageSelected) ? nsel : 0) + ((parts & kStageChunk) ? nchunk : 0);
@@ -150,9 +158,13 @@ int copy_grid(const CopyArgs& a) { return std::min(kCopyBlocks, std::max(1, 2 * 
 }  // namespace
 
 hipError_t launch_stage_copy(const Shape& s, const void* host_k, const void* host_v, void* stage_k, void* stage_v,
-                             const int32_t* pt, const int32_t* sel, int parts, bool to_host, hipStream_t st) {
+                             const int32_t* pt, const int32_t* sel, int parts, bool to_host, int src_slots,
+                             int page_lo, int page_hi, hipStream_t st) {
   CopyArgs a = copy_args(s, s.bf16 ? 2 : 4, pt, sel, parts);
   if (a.n_blocks == 0) return hipSuccess;
+  a.n_host_slots = src_slots;
+  a.page_lo = page_lo;
+  a.page_hi = page_hi;
   a.to_host = to_host ? 1 : 0;
   if (to_host) {
     a.src[0] = stage_k;

@@ -25,7 +25,9 @@ Staging is double-buffered, so the copies for one chunk run while the
 neighbouring chunk computes:
   forward   chunk i+1's selection is made before chunk i's attention (it needs
             only chunk i's representative vectors), so its gather overlaps
-            chunk i's attention.  This needs every chunk's queries up front,
+            chunk i's attention; the pages of chunk i it selects are copied
+            from chunk i's staging buffer, so the gather need not wait for
+            chunk i's offload.  This needs every chunk's queries up front,
             as in this single-layer driver; in a full model the next chunk's
             queries come from the layer below.
   backward  chunk i-1's gather and chunk i+1's gradient flush overlap chunk i's
@@ -55,7 +57,7 @@ from .step import TORCH_DTYPE
 class OffloadedSequence:
     def __init__(self, n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_chunks, top_k,
                  n_initial_pages=0, n_slots=None, dtype="bf16", softmax_scale=0.0, device="cuda",
-                 keep_activations=False, n_buffers=2):
+                 keep_activations=False, n_buffers=2, copy_cus=0):
         if chunk_len % page_size:
             raise ValueError("chunk_len must be a multiple of page_size")
         if n_buffers < 2:
@@ -107,8 +109,7 @@ class OffloadedSequence:
         ws_bwd = max(oomb_bwd_workspace_bytes(d) for d in self.staged)
         self.ws_select = torch.empty(max(ws_sel, 256), dtype=torch.uint8, device=device)
         self.ws_bwd = torch.empty(max(ws_bwd, 256), dtype=torch.uint8, device=device)
-        self.h2d = torch.cuda.Stream(device=device)
-        self.d2h = torch.cuda.Stream(device=device)
+        self._make_streams(device, copy_cus)
 
     def prior_pages(self, i):
         return self.n0 + i * self.chunk_pages
@@ -133,63 +134,84 @@ class OffloadedSequence:
         pools [n_slots][Hkv][ps][D] holding the initial context (the chunks'
         pages are written into them here); page_table: int32 [total pages] on
         the device, logical page -> host slot.  on_chunk(i, O, LSE) as in
-        ChunkedSequence.  Runs on the current stream; returns (O, LSE)."""
+        ChunkedSequence.  Ordered after, and before, the caller's current
+        stream; returns (O, LSE).  The host pools must stay allocated until
+        that work has completed."""
         hk, hv = self._views(host_k, host_v)
-        comp = torch.cuda.current_stream()
+        caller = torch.cuda.current_stream()
+        comp = self._enter(caller)
         ev = lambda: torch.cuda.Event()
         fwd_done = [None] * self.n_chunks
         offloaded = [None] * self.n_chunks
         gathered = [None] * self.n_chunks
 
-        def gather_selected(i):
+        def gather_selected(i, ready):
+            """Selected blocks of chunk i into its staging buffer: pages of
+            chunk i-1 from that chunk's staging buffer (still on the device),
+            earlier pages from the host pools."""
             b = i % self.nbuf
-            ready = ev()
-            ready.record(comp)  # selection of chunk i made
             with torch.cuda.stream(self.h2d):
-                self.h2d.wait_event(ready)
-                if i >= 1 and offloaded[i - 1] is not None:
-                    self.h2d.wait_event(offloaded[i - 1])  # chunk i-1's pages are in the host pools
+                self.h2d.wait_event(ready)  # chunk i's selection made, chunk i-1's pages staged
+                if i >= 2:
+                    self.h2d.wait_event(offloaded[i - 2])  # chunks before i-1 are in the host pools
                 if i >= self.nbuf:  # buffer b's previous chunk has run and been offloaded
                     self.h2d.wait_event(fwd_done[i - self.nbuf])
                     self.h2d.wait_event(offloaded[i - self.nbuf])
                 if self.keff(i) > 0:
-                    oomb_stage_gather(self.descs[i], hk, hv, page_table, self.sel[i], OOMB_STAGE_SELECTED,
-                                      self.stage_k[b], self.stage_v[b], stream=self.h2d)
+                    recent = self.prior_pages(i - 1) if i >= 1 else self.prior_pages(i)
+                    if recent > 0:
+                        oomb_stage_gather(self.descs[i], hk, hv, page_table, self.sel[i], OOMB_STAGE_SELECTED,
+                                          self.stage_k[b], self.stage_v[b], first_page=0, n_pages=recent,
+                                          stream=self.h2d)
+                    if i >= 1:
+                        pb = (i - 1) % self.nbuf
+                        oomb_stage_gather(self.descs[i], self.stage_k[pb], self.stage_v[pb], self._pt_rep[i - 1],
+                                          self.sel[i], OOMB_STAGE_SELECTED, self.stage_k[b], self.stage_v[b],
+                                          src_slots=self.staged[i - 1].n_slots, first_page=recent,
+                                          n_pages=self.chunk_pages, stream=self.h2d)
                 gathered[i] = ev()
                 gathered[i].record(self.h2d)
 
-        if self.n0 > 0:  # representative vectors of the initial context, read through the host view
-            oomb_rep_update(self.descs[0], hk, page_table, 0, self.n0, self.rep)
-        if self.keff(0) > 0:
-            oomb_select_topk(self.descs[0], q[0], self.rep, self.sel[0], None, self.ws_select)
-        gather_selected(0)
-        for i in range(self.n_chunks):
-            b, a = i % self.nbuf, self._act(i)
-            sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
-            nsel = self.hkv * self.keff(i)
-            if i >= self.nbuf:
-                comp.wait_event(offloaded[i - self.nbuf])  # buffer b's chunk pages are in the host pools
-            sk[nsel:nsel + self.chunk_pages].copy_(k_new[i])
-            sv[nsel:nsel + self.chunk_pages].copy_(v_new[i])
-            oomb_rep_update(self.descs[i], sk, self._pt_rep[i], self.prior_pages(i), self.chunk_pages, self.rep)
-            local = ev()
-            local.record(comp)
-            with torch.cuda.stream(self.d2h):
-                self.d2h.wait_event(local)
-                oomb_stage_offload_chunk(self.descs[i], sk, sv, page_table, hk, hv, stream=self.d2h)
-                offloaded[i] = ev()
-                offloaded[i].record(self.d2h)
-            if i + 1 < self.n_chunks:
-                if self.keff(i + 1) > 0:
-                    oomb_select_topk(self.descs[i + 1], q[i + 1], self.rep, self.sel[i + 1], None, self.ws_select)
-                gather_selected(i + 1)
-            comp.wait_event(gathered[i])
-            oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a])
-            fwd_done[i] = ev()
-            fwd_done[i].record(comp)
-            if on_chunk is not None:
-                on_chunk(i, self.o[a], self.lse[a])
-        comp.wait_event(offloaded[-1])
+        with torch.cuda.stream(comp):
+            if self.n0 > 0:  # representative vectors of the initial context, read through the host view
+                oomb_rep_update(self.descs[0], hk, page_table, 0, self.n0, self.rep, stream=comp)
+            if self.keff(0) > 0:
+                oomb_select_topk(self.descs[0], q[0], self.rep, self.sel[0], None, self.ws_select, stream=comp)
+            ready = ev()
+            ready.record(comp)
+            gather_selected(0, ready)
+            for i in range(self.n_chunks):
+                b, a = i % self.nbuf, self._act(i)
+                sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
+                nsel = self.hkv * self.keff(i)
+                if i >= self.nbuf:
+                    comp.wait_event(offloaded[i - self.nbuf])  # buffer b's chunk pages are in the host pools
+                sk[nsel:nsel + self.chunk_pages].copy_(k_new[i])
+                sv[nsel:nsel + self.chunk_pages].copy_(v_new[i])
+                oomb_rep_update(self.descs[i], sk, self._pt_rep[i], self.prior_pages(i), self.chunk_pages,
+                                self.rep, stream=comp)
+                if i + 1 < self.n_chunks and self.keff(i + 1) > 0:
+                    oomb_select_topk(self.descs[i + 1], q[i + 1], self.rep, self.sel[i + 1], None, self.ws_select,
+                                     stream=comp)
+                ready = ev()
+                ready.record(comp)
+                # chunk i's pages to the host and chunk i+1's blocks to the device,
+                # both overlapping chunk i's attention
+                with torch.cuda.stream(self.d2h):
+                    self.d2h.wait_event(ready)
+                    oomb_stage_offload_chunk(self.descs[i], sk, sv, page_table, hk, hv, stream=self.d2h)
+                    offloaded[i] = ev()
+                    offloaded[i].record(self.d2h)
+                if i + 1 < self.n_chunks:
+                    gather_selected(i + 1, ready)
+                comp.wait_event(gathered[i])
+                oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], stream=comp)
+                fwd_done[i] = ev()
+                fwd_done[i].record(comp)
+                if on_chunk is not None:
+                    on_chunk(i, self.o[a], self.lse[a])
+            comp.wait_event(offloaded[-1])
+        self._leave(comp, caller)
         return self.o, self.lse
 
     def backward(self, q, dO, host_k, host_v, host_dk, host_dv, page_table):
@@ -197,13 +219,15 @@ class OffloadedSequence:
         host_dv (pinned fp32 pools) receive the gradients in place.  The forward
         must have run (it wrote the chunks' pages into host_k / host_v); without
         kept activations each chunk's forward is re-run on its staged blocks.
-        Runs on the current stream; when it completes, host_dk / host_dv are
-        final.  Returns dQ."""
+        Ordered after, and before, the caller's current stream; once that
+        completes, host_dk / host_dv are final.  Returns dQ."""
         hk, hv, hdk, hdv = self._views(host_k, host_v, host_dk, host_dv)
-        comp = torch.cuda.current_stream()
+        caller = torch.cuda.current_stream()
+        comp = self._enter(caller)
         ev = lambda: torch.cuda.Event()
         start = ev()
         start.record(comp)  # after the forward, including its last offload
+        last = self.n_chunks - 1
         bwd_done = [None] * self.n_chunks
         flushed = [None] * self.n_chunks
         gathered = [None] * self.n_chunks
@@ -212,7 +236,7 @@ class OffloadedSequence:
             b = i % self.nbuf
             with torch.cuda.stream(self.h2d):
                 self.h2d.wait_event(start)
-                if i + self.nbuf < self.n_chunks:  # buffer b's previous chunk has run
+                if i + self.nbuf <= last:  # buffer b's previous chunk has run
                     self.h2d.wait_event(bwd_done[i + self.nbuf])
                 oomb_stage_gather(self.descs[i], hk, hv, page_table, self.sel[i],
                                   OOMB_STAGE_SELECTED | OOMB_STAGE_CHUNK, self.stage_k[b], self.stage_v[b],
@@ -220,27 +244,95 @@ class OffloadedSequence:
                 gathered[i] = ev()
                 gathered[i].record(self.h2d)
 
-        last = self.n_chunks - 1
-        gather(last)
-        for i in reversed(range(self.n_chunks)):
-            b, a = i % self.nbuf, self._act(i)
-            sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
-            comp.wait_event(gathered[i])
-            if i + self.nbuf <= last:
-                comp.wait_event(flushed[i + self.nbuf])  # gradient staging b is back at zero
-            if not self.keep_activations:
-                oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a])
-            oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
-                          self.stage_dk[b], self.stage_dv[b], self.ws_bwd)
-            bwd_done[i] = ev()
-            bwd_done[i].record(comp)
-            if i > 0:
-                gather(i - 1)
-            with torch.cuda.stream(self.d2h):
-                self.d2h.wait_event(bwd_done[i])
-                oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table, self.sel[i],
-                                       hdk, hdv, stream=self.d2h)
-                flushed[i] = ev()
-                flushed[i].record(self.d2h)
-        comp.wait_event(flushed[0])
+        with torch.cuda.stream(comp):
+            gather(last)
+            for i in reversed(range(self.n_chunks)):
+                b, a = i % self.nbuf, self._act(i)
+                sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
+                comp.wait_event(gathered[i])
+                if i + self.nbuf <= last:
+                    comp.wait_event(flushed[i + self.nbuf])  # gradient staging b is back at zero
+                if not self.keep_activations:
+                    oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], stream=comp)
+                oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
+                              self.stage_dk[b], self.stage_dv[b], self.ws_bwd, stream=comp)
+                bwd_done[i] = ev()
+                bwd_done[i].record(comp)
+                if i > 0:
+                    gather(i - 1)
+                with torch.cuda.stream(self.d2h):  # flushes in chunk order on one stream
+                    self.d2h.wait_event(bwd_done[i])
+                    oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table,
+                                           self.sel[i], hdk, hdv, stream=self.d2h)
+                    flushed[i] = ev()
+                    flushed[i].record(self.d2h)
+            comp.wait_event(flushed[0])
+        self._leave(comp, caller)
         return self.dq
+
+    # ---- streams
+
+    def _enter(self, caller):
+        """The stream the attention runs on, ordered after the caller's work."""
+        if self.comp is None:
+            return caller
+        e = torch.cuda.Event()
+        e.record(caller)
+        self.comp.wait_event(e)
+        return self.comp
+
+    def _leave(self, comp, caller):
+        if comp is not caller:
+            e = torch.cuda.Event()
+            e.record(comp)
+            caller.wait_event(e)
+
+    def _make_streams(self, device, copy_cus):
+        """Copy streams, and with copy_cus > 0 a compute stream, partitioned by
+        compute-unit masks: the copy kernels get copy_cus compute units of their
+        own (one per XCD when copy_cus is 8), the attention the rest.  Measured
+        at the Qwen2.5-7B shape, the partition costs the attention more than it
+        saves the copies (the forward kernel loses 15% with 8 units fewer), so
+        the default is none.  All streams keep the default priority."""
+        self.comp, self._owned = None, []
+        if copy_cus <= 0:
+            self.h2d = torch.cuda.Stream(device=device)
+            self.d2h = torch.cuda.Stream(device=device)
+            return
+        import ctypes
+        from . import hip_runtimes_loaded
+        n_cu = torch.cuda.get_device_properties(device).multi_processor_count
+        if copy_cus >= n_cu:
+            raise ValueError("copy_cus must leave compute units for the attention")
+        words = (n_cu + 31) // 32
+        # CU i + (n_cu/copy_cus)*i + ... : spread over the chip whether the mask
+        # bits run XCD-major or XCD-interleaved
+        step = n_cu // copy_cus
+        picks = {(k * step + k) % n_cu for k in range(copy_cus)}
+        copy_mask, comp_mask = [0] * words, [0] * words
+        for c in range(n_cu):
+            m = copy_mask if c in picks else comp_mask
+            m[c // 32] |= 1 << (c % 32)
+        self._rt = ctypes.CDLL(hip_runtimes_loaded()[0])
+
+        def create(mask):
+            st = ctypes.c_void_p()
+            arr = (ctypes.c_uint32 * words)(*mask)
+            rc = self._rt.hipExtStreamCreateWithCUMask(ctypes.byref(st), ctypes.c_uint32(words), arr)
+            if rc != 0:
+                raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with hipError {rc}")
+            self._owned.append(st.value)
+            return torch.cuda.ExternalStream(st.value, device=device)
+
+        with torch.cuda.device(device):
+            self.comp = create(comp_mask)
+            self.h2d = create(copy_mask)
+            self.d2h = create(copy_mask)
+
+    def __del__(self):
+        import ctypes
+        for st in getattr(self, "_owned", []):
+            try:
+                self._rt.hipStreamDestroy(ctypes.c_void_p(st))
+            except Exception:
+                pass

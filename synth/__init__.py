@@ -191,6 +191,7 @@ class Sequence:
 # Whole sequences of the Qwen2.5-7B attention shape, chunk by chunk (name -> (seed, Sequence)).
 SEQUENCES = {
     "seq-64k": (6, Sequence(hq=28, hkv=4, d=128, ps=128, c=4096, chunks=16, k=64)),
+    "seq-256k": (7, Sequence(hq=28, hkv=4, d=128, ps=128, c=4096, chunks=64, k=64)),
 }
 
 

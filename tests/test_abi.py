@@ -159,11 +159,15 @@ def test_stage_desc():
 def test_stage_calls_reject_bad_arguments():
     d = P.ctypes.byref(good())
     L = P._L
-    assert L.oomb_stage_gather(d, A, A, A, A, 0, A, A, None) == BAD_SHAPE          # no part
-    assert L.oomb_stage_gather(d, A, A, A, A, 4, A, A, None) == BAD_SHAPE          # unknown part
-    assert L.oomb_stage_gather(d, None, A, A, A, 3, A, A, None) == NULL_PTR
-    assert L.oomb_stage_gather(d, A, A, A, None, 1, A, A, None) == NULL_PTR        # selection needed
-    assert L.oomb_stage_gather(d, A + 4, A, A, A, 3, A, A, None) == MISALIGNED
+    g = lambda src=A, slots=2080, sel=A, parts=3, first=0, n=2048: L.oomb_stage_gather(
+        d, src, A, slots, A, sel, parts, first, n, A, A, None)
+    assert g(parts=0) == BAD_SHAPE                                  # no part
+    assert g(parts=4) == BAD_SHAPE                                  # unknown part
+    assert g(slots=0) == BAD_SHAPE
+    assert g(first=-1) == BAD_SHAPE and g(n=-1) == BAD_SHAPE
+    assert g(src=None) == NULL_PTR
+    assert g(sel=None, parts=1) == NULL_PTR                         # selection needed
+    assert g(src=A + 4) == MISALIGNED
     assert L.oomb_stage_offload_chunk(d, A, A, A, None, A, None) == NULL_PTR
     assert L.oomb_stage_flush_grads(d, A, A, A, None, A, A, None) == NULL_PTR
     assert L.oomb_stage_flush_grads(d, A, A, A, A, A, A + 8, None) == MISALIGNED

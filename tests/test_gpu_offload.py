@@ -11,7 +11,9 @@
    - against the whole-sequence fp64 oracle, element by element;
    - the host K/V pools end up holding every chunk's pages bit for bit (they
      start poisoned with NaN there, so only the offload can fill them);
-   - two and three staging buffers give bitwise the same results.
+   - two and three staging buffers, kept or recomputed activations, and copy
+     streams with or without their own compute units give bitwise the same
+     results.
 """
 from __future__ import annotations
 
@@ -129,7 +131,7 @@ def test_stage_copy_kernels(dtype):
 
 # ------------------------------------------------------------- 2. sequences
 
-def run_offloaded(s, seed, keep=False, nbuf=2):
+def run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8):
     from paged_sparse_attention_amd.offload import OffloadedSequence
     x = synth.make_sequence_inputs(s, seed)
     last = s.step(s.chunks - 1)
@@ -146,7 +148,7 @@ def run_offloaded(s, seed, keep=False, nbuf=2):
     dk0, dv0 = synth.canary(last, seed, "k"), synth.canary(last, seed, "v")
     host_dk, host_dv = pinned(dk0), pinned(dv0)
     drv = OffloadedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                            softmax_scale=s.scale, keep_activations=keep, n_buffers=nbuf)
+                            softmax_scale=s.scale, keep_activations=keep, n_buffers=nbuf, copy_cus=copy_cus)
     outs = []
     pt_d = H.dev(pt)
     drv.forward(q, k_new, v_new, host_k, host_v, pt_d,
@@ -193,11 +195,11 @@ def test_offloaded_sequence(ora, name):
     H.say(f"  {json.dumps(report, default=float)}")
 
 
-def test_offload_buffer_count_and_activations_do_not_change_results():
+def test_offload_buffers_streams_and_activations_do_not_change_results():
     seed, s = SEQ["seq-qwen-shape"]
-    H.say(f"case seq-qwen-shape offloaded, 2 vs 3 staging buffers: {s}")
-    _, a, outs_a, _, _, dk_a, dv_a = run_offloaded(s, seed, keep=False, nbuf=2)
-    _, b, outs_b, _, _, dk_b, dv_b = run_offloaded(s, seed, keep=True, nbuf=3)
+    H.say(f"case seq-qwen-shape offloaded, 2 vs 3 staging buffers, masked vs unmasked streams: {s}")
+    _, a, outs_a, _, _, dk_a, dv_a = run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8)
+    _, b, outs_b, _, _, dk_b, dv_b = run_offloaded(s, seed, keep=True, nbuf=3, copy_cus=0)
     for i in range(s.chunks):
         assert torch.equal(outs_a[i][0], outs_b[i][0]) and torch.equal(outs_a[i][1], outs_b[i][1]), f"chunk {i}"
         assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ"
