@@ -227,7 +227,8 @@ def sequence_bench(args):
         del k, v, dk, dv, drv
         torch.cuda.empty_cache()
         off = OffloadedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                                softmax_scale=s.scale, keep_activations=keep, copy_cus=args.copy_cus)
+                                softmax_scale=s.scale, keep_activations=keep, copy_cus=args.copy_cus,
+                                host_accumulate=args.host_accumulate)
         ms, fwd_ms, bwd_ms = _time_passes(
             args, lambda: off.forward(q, k_new, v_new, host_k, host_v, pt),
             lambda: off.backward(q, do, host_k, host_v, host_dk, host_dv, pt), hip_path)
@@ -238,9 +239,11 @@ def sequence_bench(args):
             h2d += 2 * s.hkv * ke * blk * eb                          # forward: selected K/V blocks
             d2h += 2 * cp * blk * eb                                  # forward: the chunk's K/V pages
             h2d += 2 * (s.hkv * ke + cp) * blk * eb                   # backward: selected and chunk K/V
-            h2d += 2 * (s.hkv * ke + cp) * blk * 4                    # backward: host dK/dV read ...
-            d2h += 2 * (s.hkv * ke + cp) * blk * 4                    # ... and written back
+            if not args.host_accumulate:
+                h2d += 2 * (s.hkv * ke + cp) * blk * 4                # backward: host dK/dV read ...
+            d2h += 2 * (s.hkv * ke + cp) * blk * 4                    # ... and written back (or the deltas)
         offload = {"overhead_vs_resident": ms / resident["ms_per_step"] - 1.0, "copy_cus": args.copy_cus,
+                   "gradient_adds": "host" if args.host_accumulate else "device, over the link",
                    "host_to_device_bytes_per_step": h2d, "device_to_host_bytes_per_step": d2h,
                    "host_pool_bytes": 2 * host_k.numel() * eb + 2 * host_dk.numel() * 4,
                    "device_staging_bytes": sum(t.numel() * t.element_size()
@@ -290,6 +293,8 @@ def main():
                          "resident driver is timed too, for the overhead")
     ap.add_argument("--copy-cus", type=int, default=0,
                     help="with --offload: compute units reserved for the copy kernels (0: no partition)")
+    ap.add_argument("--host-accumulate", action="store_true",
+                    help="with --offload: add the gradients on the host CPU instead of on the device over the link")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()

@@ -219,6 +219,28 @@ int oomb_stage_flush_grads(const oomb_desc* desc, float* stage_dk, float* stage_
                            const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
                            void* stream);
 
+/* Gradients out (fp32): the staged gradient blocks of the step, in the
+ * staging layout's block order -- block b < Hkv*K_eff is kv-head b / K_eff's
+ * block of slot b, block Hkv*K_eff + j*Hkv + h is kv-head h of the chunk's
+ * page j -- are written to out_dk / out_dv as n_blocks = Hkv*K_eff + (C/ps)*Hkv
+ * consecutive blocks of ps*D floats (normally the device view of pinned host
+ * buffers), and those staged blocks are then set to zero.  With
+ * oomb_host_accumulate_grads this replaces oomb_stage_flush_grads: the link
+ * carries the gradients one way instead of there and back. */
+int oomb_stage_grads_out(const oomb_desc* desc, float* stage_dk, float* stage_dv, float* out_dk, float* out_dv,
+                         void* stream);
+
+/* Host accumulation (host memory only, no HIP call, returns when done): for
+ * each block b of oomb_stage_grads_out's order, host_dk[slot][h] += delta_dk[b]
+ * and host_dv[slot][h] += delta_dv[b], where (slot, h) is the host-pool block
+ * that b stands for: page_table[sel[h][k]] or page_table[N + j].  page_table
+ * and sel are HOST arrays.  Entries out of range are skipped.  Runs on
+ * n_threads host threads (0 or 1: the calling thread only); each element gets
+ * one fp32 add, so the result equals oomb_stage_flush_grads'. */
+int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delta_dk, const float* delta_dv,
+                               const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
+                               int32_t n_threads);
+
 /* Static text for a status code (host). */
 const char* oomb_status_string(int status);
 

@@ -66,6 +66,8 @@ def _load():
         "oomb_stage_gather": (ctypes.c_int, [P, vp, vp, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "oomb_stage_offload_chunk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp]),
         "oomb_stage_flush_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
+        "oomb_stage_grads_out": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "oomb_host_accumulate_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, i32]),
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "oomb_abi_version": (ctypes.c_int, []),
         "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -194,6 +196,22 @@ def oomb_stage_offload_chunk(desc, stage_k, stage_v, page_table, host_k, host_v,
 def oomb_stage_flush_grads(desc, stage_dk, stage_dv, page_table, sel, host_dk, host_dv, stream=None):
     _check(_L.oomb_stage_flush_grads(ctypes.byref(desc), _ptr(stage_dk), _ptr(stage_dv), _ptr(page_table), _ptr(sel),
                                      _ptr(host_dk), _ptr(host_dv), _stream(stream)))
+
+
+def oomb_stage_grads_out(desc, stage_dk, stage_dv, out_dk, out_dv, stream=None):
+    """out_dk / out_dv: device views (oomb_host_view) of pinned host buffers, or device buffers."""
+    _check(_L.oomb_stage_grads_out(ctypes.byref(desc), _ptr(stage_dk), _ptr(stage_dv), _ptr(out_dk), _ptr(out_dv),
+                                   _stream(stream)))
+
+
+def oomb_host_accumulate_grads(desc, delta_dk, delta_dv, page_table, sel, host_dk, host_dv, n_threads=8):
+    """Every argument is host memory (CPU tensors); returns when done.  The GIL
+    is released during the call."""
+    for t in (delta_dk, delta_dv, page_table, sel, host_dk, host_dv):
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            raise ValueError("oomb_host_accumulate_grads takes host tensors")
+    _check(_L.oomb_host_accumulate_grads(ctypes.byref(desc), _ptr(delta_dk), _ptr(delta_dv), _ptr(page_table),
+                                         _ptr(sel), _ptr(host_dk), _ptr(host_dv), n_threads))
 
 
 def oomb_trace_events(events, capacity=None):

@@ -239,6 +239,29 @@ OOMB_API int oomb_stage_flush_grads(const oomb_desc* desc, float* stage_dk, floa
       oomb::launch_grad_flush(s, stage_dk, stage_dv, host_dk, host_dv, page_table, sel, (hipStream_t)stream));
 }
 
+OOMB_API int oomb_stage_grads_out(const oomb_desc* desc, float* stage_dk, float* stage_dv, float* out_dk,
+                                  float* out_dv, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({stage_dk, stage_dv, out_dk, out_dv}))) return rc;
+  (void)hipGetLastError();
+  return launched(oomb::launch_grads_out(s, stage_dk, stage_dv, out_dk, out_dv, (hipStream_t)stream));
+}
+
+OOMB_API int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delta_dk, const float* delta_dv,
+                                        const int32_t* page_table, const int32_t* sel, float* host_dk,
+                                        float* host_dv, int32_t n_threads) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if (!delta_dk || !delta_dv || !page_table || !host_dk || !host_dv) return OOMB_ERR_NULL_PTR;
+  if (s.keff > 0 && !sel) return OOMB_ERR_NULL_PTR;
+  if (n_threads < 0 || n_threads > 256) return OOMB_ERR_BAD_SHAPE;
+  oomb::host_accumulate_grads(s, delta_dk, delta_dv, page_table, sel, host_dk, host_dv, n_threads);
+  return OOMB_OK;
+}
+
 OOMB_API const char* oomb_status_string(int status) {
   switch (status) {
     case OOMB_OK: return "ok";

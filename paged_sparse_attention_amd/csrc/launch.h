@@ -70,6 +70,10 @@ hipError_t launch_stage_copy(const Shape& s, const void* host_k, const void* hos
                              int page_lo, int page_hi, hipStream_t st);
 hipError_t launch_grad_flush(const Shape& s, float* stage_dk, float* stage_dv, float* host_dk, float* host_dv,
                              const int32_t* pt, const int32_t* sel, hipStream_t st);
+hipError_t launch_grads_out(const Shape& s, float* stage_dk, float* stage_dv, float* out_dk, float* out_dv,
+                            hipStream_t st);
 hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st);
+void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
+                           const int32_t* sel, float* host_dk, float* host_dv, int n_threads);
 
 }  // namespace oomb

@@ -20,6 +20,10 @@
 // its own outstanding requests.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <thread>
+#include <vector>
+
 #include "launch.h"
 #include "trace.h"
 
@@ -130,6 +134,50 @@ __global__ __launch_bounds__(kCopyThreads) void grad_flush_kernel(CopyArgs a) {
   }
 }
 
+// Gradients out: staged block b (the staging layout's block order: selected
+// blocks, then the chunk's pages kv-head by kv-head) -> block b of a compact
+// buffer (host memory), then the staged block is set to zero.
+__global__ __launch_bounds__(kCopyThreads) void grad_out_kernel(CopyArgs a) {
+  const int items = 2 * a.n_blocks;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int t = it & 1, b = it >> 1;
+    const int nsel = a.hkv * a.keff;
+    int ss, h;
+    if (b < nsel) {
+      h = b / a.keff;
+      ss = b;
+    } else {
+      h = (b - nsel) % a.hkv;
+      ss = nsel + (b - nsel) / a.hkv;
+    }
+    int4* __restrict__ st = (int4*)a.src[t] + ((int64_t)ss * a.hkv + h) * a.vec_per_block;
+    int4* __restrict__ d = (int4*)a.dst[t] + (int64_t)b * a.vec_per_block;
+    const int n = a.vec_per_block;
+    const int4 z = make_int4(0, 0, 0, 0);
+    for (int i = threadIdx.x; i < n; i += kCopyThreads * kCopyUnroll) {
+      int4 r0, r1, r2, r3;
+      r0 = st[i];
+      if (i + kCopyThreads < n) r1 = st[i + kCopyThreads];
+      if (i + 2 * kCopyThreads < n) r2 = st[i + 2 * kCopyThreads];
+      if (i + 3 * kCopyThreads < n) r3 = st[i + 3 * kCopyThreads];
+      d[i] = r0;
+      st[i] = z;
+      if (i + kCopyThreads < n) {
+        d[i + kCopyThreads] = r1;
+        st[i + kCopyThreads] = z;
+      }
+      if (i + 2 * kCopyThreads < n) {
+        d[i + 2 * kCopyThreads] = r2;
+        st[i + 2 * kCopyThreads] = z;
+      }
+      if (i + 3 * kCopyThreads < n) {
+        d[i + 3 * kCopyThreads] = r3;
+        st[i + 3 * kCopyThreads] = z;
+      }
+    }
+  }
+}
+
 __global__ void stage_tables_kernel(int32_t* sel_stage, int nsel, int32_t* pt_stage, int n_stage) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nsel) sel_stage[i] = i;
@@ -195,11 +243,67 @@ hipError_t launch_grad_flush(const Shape& s, float* stage_dk, float* stage_dv, f
   return hipGetLastError();
 }
 
+hipError_t launch_grads_out(const Shape& s, float* stage_dk, float* stage_dv, float* out_dk, float* out_dv,
+                            hipStream_t st) {
+  CopyArgs a = copy_args(s, 4, nullptr, nullptr, kStageSelected | kStageChunk);
+  if (a.n_blocks == 0) return hipSuccess;
+  a.src[0] = stage_dk;
+  a.src[1] = stage_dv;
+  a.dst[0] = out_dk;
+  a.dst[1] = out_dv;
+  Traced tr(st, "grad_out_kernel");
+  hipLaunchKernelGGL(grad_out_kernel, dim3(copy_grid(a)), dim3(kCopyThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st) {
   const int nsel = s.hkv * s.keff, n_stage = nsel + s.c / s.ps;
   hipLaunchKernelGGL(stage_tables_kernel, dim3((n_stage + 255) / 256), dim3(256), 0, st, sel_stage, nsel, pt_stage,
                      n_stage);
   return hipGetLastError();
+}
+
+// Host side of the gradient offload: compact block b of delta is added to its
+// (host slot, kv-head) block of the host pool.  Within one call every
+// destination block is distinct (a kv-head's selected pages are distinct and
+// none is a chunk page), so the threads never write the same element.
+void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
+                           const int32_t* sel, float* host_dk, float* host_dv, int n_threads) {
+  const int nsel = s.hkv * s.keff, n_blocks = nsel + (s.c / s.ps) * s.hkv;
+  const int64_t blk = (int64_t)s.ps * s.d;
+  auto work = [&](int b0, int b1) {
+    for (int b = b0; b < b1; ++b) {
+      int h, logical;
+      if (b < nsel) {
+        h = b / s.keff;
+        logical = sel[b];
+        if (logical < 0 || logical >= s.n) continue;
+      } else {
+        h = (b - nsel) % s.hkv;
+        logical = s.n + (b - nsel) / s.hkv;
+      }
+      const int slot = pt[logical];
+      if (slot < 0 || slot >= s.n_slots) continue;
+      const int64_t off = ((int64_t)slot * s.hkv + h) * blk;
+      const float* dk = delta_dk + (int64_t)b * blk;
+      const float* dv = delta_dv + (int64_t)b * blk;
+      float* hk = host_dk + off;
+      float* hv = host_dv + off;
+      for (int64_t i = 0; i < blk; ++i) hk[i] += dk[i];
+      for (int64_t i = 0; i < blk; ++i) hv[i] += dv[i];
+    }
+  };
+  const int nt = std::max(1, std::min(n_threads, n_blocks));
+  if (nt == 1) {
+    work(0, n_blocks);
+    return;
+  }
+  std::vector<std::thread> pool;
+  pool.reserve(nt - 1);
+  for (int t = 1; t < nt; ++t)
+    pool.emplace_back(work, (int)((int64_t)n_blocks * t / nt), (int)((int64_t)n_blocks * (t + 1) / nt));
+  work(0, (int)((int64_t)n_blocks / nt));
+  for (std::thread& th : pool) th.join();
 }
 
 }  // namespace oomb

@@ -19,7 +19,15 @@ activations.  Three streams carry the work:
            chunk's own pages) from the host pools into a staging buffer
   d2h      oomb_stage_offload_chunk after a chunk's forward (its keys and
            values to the host pools) and oomb_stage_flush_grads after its
-           backward (host dK/dV += staged gradients, staging cleared)
+           backward (the device adds the staged gradients into the host dK/dV
+           pools over the link and clears the staging); with
+           host_accumulate=True instead oomb_stage_grads_out (the staged
+           gradients to a pinned host buffer, staging cleared), which a host
+           worker thread adds into the pools with oomb_host_accumulate_grads
+           while the device runs the next chunk.  Both give the same bits; the
+           device flush measured faster at the Qwen2.5-7B shape (the link
+           traffic slows the concurrent attention kernels whichever way it
+           flows, and the host route adds the host's memory traffic)
 
 Staging is double-buffered, so the copies for one chunk run while the
 neighbouring chunk computes:
@@ -45,19 +53,21 @@ Marshalling and stream ordering only: every step runs in the library's kernels.
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import torch
 
 from . import (OOMB_STAGE_CHUNK, OOMB_STAGE_SELECTED, make_desc, oomb_attn_bwd, oomb_attn_fwd,
-               oomb_bwd_workspace_bytes, oomb_host_view, oomb_rep_update, oomb_select_topk,
-               oomb_select_workspace_bytes, oomb_stage_desc, oomb_stage_flush_grads, oomb_stage_gather,
-               oomb_stage_offload_chunk, oomb_stage_tables)
+               oomb_bwd_workspace_bytes, oomb_host_accumulate_grads, oomb_host_view, oomb_rep_update,
+               oomb_select_topk, oomb_select_workspace_bytes, oomb_stage_desc, oomb_stage_flush_grads,
+               oomb_stage_gather, oomb_stage_grads_out, oomb_stage_offload_chunk, oomb_stage_tables)
 from .step import TORCH_DTYPE
 
 
 class OffloadedSequence:
     def __init__(self, n_q_heads, n_kv_heads, head_dim, page_size, chunk_len, n_chunks, top_k,
                  n_initial_pages=0, n_slots=None, dtype="bf16", softmax_scale=0.0, device="cuda",
-                 keep_activations=False, n_buffers=2, copy_cus=0):
+                 keep_activations=False, n_buffers=2, copy_cus=0, host_accumulate=False, host_threads=12):
         if chunk_len % page_size:
             raise ValueError("chunk_len must be a multiple of page_size")
         if n_buffers < 2:
@@ -65,6 +75,7 @@ class OffloadedSequence:
         self.hq, self.hkv, self.d, self.ps, self.c = n_q_heads, n_kv_heads, head_dim, page_size, chunk_len
         self.n_chunks, self.top_k, self.n0, self.dtype = n_chunks, top_k, n_initial_pages, dtype
         self.keep_activations, self.nbuf = keep_activations, n_buffers
+        self.host_accumulate, self.host_threads = host_accumulate, host_threads
         self.chunk_pages = chunk_len // page_size
         self.total_pages = n_initial_pages + n_chunks * self.chunk_pages
         self.n_slots = self.total_pages if n_slots is None else n_slots
@@ -109,6 +120,16 @@ class OffloadedSequence:
         ws_bwd = max(oomb_bwd_workspace_bytes(d) for d in self.staged)
         self.ws_select = torch.empty(max(ws_sel, 256), dtype=torch.uint8, device=device)
         self.ws_bwd = torch.empty(max(ws_bwd, 256), dtype=torch.uint8, device=device)
+        # host side of the gradient offload: two compact delta buffers that
+        # the device writes in turn, and host copies of the page table and of
+        # the selections (made on the compute stream during the forward)
+        n_blocks = max(self.hkv * self.keff(i) + self.chunk_pages * self.hkv for i in range(n_chunks))
+        if host_accumulate:
+            self.delta_dk = [torch.empty((n_blocks, page_size, head_dim), dtype=torch.float32).pin_memory()
+                             for _ in range(2)]
+            self.delta_dv = [torch.empty_like(t).pin_memory() for t in self.delta_dk]
+        self.sel_host = [torch.zeros(tuple(t.shape), dtype=torch.int32).pin_memory() for t in self.sel]
+        self.pt_host = torch.zeros(self.total_pages, dtype=torch.int32).pin_memory()
         self._make_streams(device, copy_cus)
 
     def prior_pages(self, i):
@@ -173,10 +194,12 @@ class OffloadedSequence:
                 gathered[i].record(self.h2d)
 
         with torch.cuda.stream(comp):
+            self.pt_host.copy_(page_table[:self.total_pages], non_blocking=True)
             if self.n0 > 0:  # representative vectors of the initial context, read through the host view
                 oomb_rep_update(self.descs[0], hk, page_table, 0, self.n0, self.rep, stream=comp)
             if self.keff(0) > 0:
                 oomb_select_topk(self.descs[0], q[0], self.rep, self.sel[0], None, self.ws_select, stream=comp)
+                self.sel_host[0].copy_(self.sel[0], non_blocking=True)
             ready = ev()
             ready.record(comp)
             gather_selected(0, ready)
@@ -193,6 +216,7 @@ class OffloadedSequence:
                 if i + 1 < self.n_chunks and self.keff(i + 1) > 0:
                     oomb_select_topk(self.descs[i + 1], q[i + 1], self.rep, self.sel[i + 1], None, self.ws_select,
                                      stream=comp)
+                    self.sel_host[i + 1].copy_(self.sel[i + 1], non_blocking=True)
                 ready = ev()
                 ready.record(comp)
                 # chunk i's pages to the host and chunk i+1's blocks to the device,
@@ -217,10 +241,12 @@ class OffloadedSequence:
     def backward(self, q, dO, host_k, host_v, host_dk, host_dv, page_table):
         """Chunks in reverse order with their forward selections; host_dk and
         host_dv (pinned fp32 pools) receive the gradients in place.  The forward
-        must have run (it wrote the chunks' pages into host_k / host_v); without
-        kept activations each chunk's forward is re-run on its staged blocks.
-        Ordered after, and before, the caller's current stream; once that
-        completes, host_dk / host_dv are final.  Returns dQ."""
+        must have run with the same page table (it wrote the chunks' pages into
+        host_k / host_v); without kept activations each chunk's forward is
+        re-run on its staged blocks.  Ordered after, and before, the caller's
+        current stream.  With host accumulation the host gradients are final
+        when this returns; otherwise once that stream's work completes.
+        Returns dQ."""
         hk, hv, hdk, hdv = self._views(host_k, host_v, host_dk, host_dv)
         caller = torch.cuda.current_stream()
         comp = self._enter(caller)
@@ -229,8 +255,10 @@ class OffloadedSequence:
         start.record(comp)  # after the forward, including its last offload
         last = self.n_chunks - 1
         bwd_done = [None] * self.n_chunks
-        flushed = [None] * self.n_chunks
+        cleared = [None] * self.n_chunks   # chunk's gradient staging read out and zeroed
         gathered = [None] * self.n_chunks
+        if self.host_accumulate:
+            dviews = [self._views(self.delta_dk[j], self.delta_dv[j]) for j in range(2)]
 
         def gather(i):
             b = i % self.nbuf
@@ -244,6 +272,18 @@ class OffloadedSequence:
                 gathered[i] = ev()
                 gathered[i].record(self.h2d)
 
+        def accumulate(i):
+            # on the worker thread: once chunk i's gradient blocks have reached
+            # host memory, add them into the host pools (the GIL is released
+            # during the add, so the main thread keeps enqueuing)
+            cleared[i].synchronize()
+            j = i % 2
+            oomb_host_accumulate_grads(self.descs[i], self.delta_dk[j], self.delta_dv[j], self.pt_host,
+                                       self.sel_host[i], host_dk, host_dv, self.host_threads)
+
+        adds = {}
+        worker = ThreadPoolExecutor(max_workers=1) if self.host_accumulate else None
+
         with torch.cuda.stream(comp):
             gather(last)
             for i in reversed(range(self.n_chunks)):
@@ -251,7 +291,7 @@ class OffloadedSequence:
                 sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
                 comp.wait_event(gathered[i])
                 if i + self.nbuf <= last:
-                    comp.wait_event(flushed[i + self.nbuf])  # gradient staging b is back at zero
+                    comp.wait_event(cleared[i + self.nbuf])  # gradient staging b is back at zero
                 if not self.keep_activations:
                     oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], stream=comp)
                 oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
@@ -260,13 +300,25 @@ class OffloadedSequence:
                 bwd_done[i].record(comp)
                 if i > 0:
                     gather(i - 1)
-                with torch.cuda.stream(self.d2h):  # flushes in chunk order on one stream
+                if self.host_accumulate and i + 2 in adds:
+                    adds.pop(i + 2).result()  # delta buffer i % 2 has been added on the host
+                with torch.cuda.stream(self.d2h):  # in chunk order on one stream
                     self.d2h.wait_event(bwd_done[i])
-                    oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table,
-                                           self.sel[i], hdk, hdv, stream=self.d2h)
-                    flushed[i] = ev()
-                    flushed[i].record(self.d2h)
-            comp.wait_event(flushed[0])
+                    if self.host_accumulate:
+                        oomb_stage_grads_out(self.descs[i], self.stage_dk[b], self.stage_dv[b], *dviews[i % 2],
+                                             stream=self.d2h)
+                    else:
+                        oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table,
+                                               self.sel[i], hdk, hdv, stream=self.d2h)
+                    cleared[i] = ev()
+                    cleared[i].record(self.d2h)
+                if self.host_accumulate:
+                    adds[i] = worker.submit(accumulate, i)  # runs while the device computes chunk i-1
+            if self.host_accumulate:
+                for i in sorted(adds, reverse=True):
+                    adds.pop(i).result()
+                worker.shutdown()
+            comp.wait_event(cleared[0])
         self._leave(comp, caller)
         return self.dq
 
@@ -294,45 +346,50 @@ class OffloadedSequence:
         at the Qwen2.5-7B shape, the partition costs the attention more than it
         saves the copies (the forward kernel loses 15% with 8 units fewer), so
         the default is none.  All streams keep the default priority."""
-        self.comp, self._owned = None, []
+        self.comp = None
         if copy_cus <= 0:
             self.h2d = torch.cuda.Stream(device=device)
             self.d2h = torch.cuda.Stream(device=device)
             return
-        import ctypes
-        from . import hip_runtimes_loaded
-        n_cu = torch.cuda.get_device_properties(device).multi_processor_count
-        if copy_cus >= n_cu:
-            raise ValueError("copy_cus must leave compute units for the attention")
-        words = (n_cu + 31) // 32
-        # CU i + (n_cu/copy_cus)*i + ... : spread over the chip whether the mask
-        # bits run XCD-major or XCD-interleaved
-        step = n_cu // copy_cus
-        picks = {(k * step + k) % n_cu for k in range(copy_cus)}
-        copy_mask, comp_mask = [0] * words, [0] * words
-        for c in range(n_cu):
-            m = copy_mask if c in picks else comp_mask
-            m[c // 32] |= 1 << (c % 32)
-        self._rt = ctypes.CDLL(hip_runtimes_loaded()[0])
+        self.comp, self.h2d, self.d2h = _masked_streams(torch.device(device), copy_cus)
 
-        def create(mask):
-            st = ctypes.c_void_p()
-            arr = (ctypes.c_uint32 * words)(*mask)
-            rc = self._rt.hipExtStreamCreateWithCUMask(ctypes.byref(st), ctypes.c_uint32(words), arr)
-            if rc != 0:
-                raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with hipError {rc}")
-            self._owned.append(st.value)
-            return torch.cuda.ExternalStream(st.value, device=device)
 
-        with torch.cuda.device(device):
-            self.comp = create(comp_mask)
-            self.h2d = create(copy_mask)
-            self.d2h = create(copy_mask)
+# Compute-unit-masked streams, made once per (device, copy_cus) and kept for
+# the life of the process: torch records events on the streams that pinned
+# host tensors were copied on when it frees them, so such a stream must
+# outlive every tensor that may have touched it.
+_MASKED = {}
 
-    def __del__(self):
-        import ctypes
-        for st in getattr(self, "_owned", []):
-            try:
-                self._rt.hipStreamDestroy(ctypes.c_void_p(st))
-            except Exception:
-                pass
+
+def _masked_streams(device, copy_cus):
+    import ctypes
+    from . import hip_runtimes_loaded
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    key = (idx, copy_cus)
+    if key in _MASKED:
+        return _MASKED[key]
+    n_cu = torch.cuda.get_device_properties(idx).multi_processor_count
+    if copy_cus >= n_cu:
+        raise ValueError("copy_cus must leave compute units for the attention")
+    words = (n_cu + 31) // 32
+    # CU k*(n_cu/copy_cus) + k: spread over the chip whether the mask bits run
+    # XCD-major or XCD-interleaved
+    step = n_cu // copy_cus
+    picks = {(k * step + k) % n_cu for k in range(copy_cus)}
+    copy_mask, comp_mask = [0] * words, [0] * words
+    for c in range(n_cu):
+        m = copy_mask if c in picks else comp_mask
+        m[c // 32] |= 1 << (c % 32)
+    rt = ctypes.CDLL(hip_runtimes_loaded()[0])
+
+    def create(mask):
+        st = ctypes.c_void_p()
+        arr = (ctypes.c_uint32 * words)(*mask)
+        rc = rt.hipExtStreamCreateWithCUMask(ctypes.byref(st), ctypes.c_uint32(words), arr)
+        if rc != 0:
+            raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with hipError {rc}")
+        return torch.cuda.ExternalStream(st.value, device=idx)
+
+    with torch.cuda.device(idx):
+        _MASKED[key] = (create(comp_mask), create(copy_mask), create(copy_mask))
+    return _MASKED[key]

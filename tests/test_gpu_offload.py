@@ -1,8 +1,9 @@
 """CPU offloading of the KV cache and its gradients, through the C ABI.
 
 1. The staging copy kernels (oomb_stage_gather, oomb_stage_offload_chunk,
-   oomb_stage_flush_grads) against the same block moves done with numpy on the
-   host: bit-exact, including the blocks they must leave alone.
+   oomb_stage_flush_grads, oomb_stage_grads_out) and the host-side
+   oomb_host_accumulate_grads against the same block moves done with numpy:
+   bit-exact, including the blocks they must leave alone.
 2. OffloadedSequence (K/V and dK/dV pools in pinned host memory, staging on the
    device, three streams) over whole sequences:
    - against the resident ChunkedSequence: selections, O, LSE and dQ bitwise;
@@ -11,9 +12,9 @@
    - against the whole-sequence fp64 oracle, element by element;
    - the host K/V pools end up holding every chunk's pages bit for bit (they
      start poisoned with NaN there, so only the offload can fill them);
-   - two and three staging buffers, kept or recomputed activations, and copy
-     streams with or without their own compute units give bitwise the same
-     results.
+   - two and three staging buffers, kept or recomputed activations, copy
+     streams with or without their own compute units, and gradients added on
+     the host or over the link by the device give bitwise the same results.
 """
 from __future__ import annotations
 
@@ -128,10 +129,26 @@ def test_stage_copy_kernels(dtype):
     assert np.array_equal(gk.numpy(), ek) and np.array_equal(gv.numpy(), ev), "flushed host gradients"
     assert np.array_equal(sdk.cpu().numpy(), esk) and np.array_equal(sdv.cpu().numpy(), esv), "cleared staging"
 
+    # gradients out to a compact host buffer, then added on the host: the same
+    # host pools as the flush, and the same cleared staging
+    nb = nsel + (c // ps) * hkv
+    out_k = pinned(np.full((nb, ps, d), np.nan, np.float32))
+    out_v = pinned(np.full((nb, ps, d), np.nan, np.float32))
+    sdk, sdv = H.dev(s0k), H.dev(s0v)
+    P.oomb_stage_grads_out(desc, sdk, sdv, P.oomb_host_view(out_k), P.oomb_host_view(out_v))
+    torch.cuda.synchronize()
+    want_k = np.stack([s0k[b, b // k] for b in range(nsel)] + [s0k[nsel + j // hkv, j % hkv] for j in range(nb - nsel)])
+    want_v = np.stack([s0v[b, b // k] for b in range(nsel)] + [s0v[nsel + j // hkv, j % hkv] for j in range(nb - nsel)])
+    assert np.array_equal(out_k.numpy(), want_k) and np.array_equal(out_v.numpy(), want_v), "gradient blocks out"
+    assert np.array_equal(sdk.cpu().numpy(), esk) and np.array_equal(sdv.cpu().numpy(), esv), "cleared staging (out)"
+    gk2, gv2 = torch.from_numpy(g0k.copy()), torch.from_numpy(g0v.copy())
+    P.oomb_host_accumulate_grads(desc, out_k, out_v, torch.from_numpy(pt), torch.from_numpy(sel), gk2, gv2, 4)
+    assert np.array_equal(gk2.numpy(), ek) and np.array_equal(gv2.numpy(), ev), "host-accumulated gradients"
+
 
 # ------------------------------------------------------------- 2. sequences
 
-def run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8):
+def run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8, host_acc=False):
     from paged_sparse_attention_amd.offload import OffloadedSequence
     x = synth.make_sequence_inputs(s, seed)
     last = s.step(s.chunks - 1)
@@ -148,7 +165,8 @@ def run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8):
     dk0, dv0 = synth.canary(last, seed, "k"), synth.canary(last, seed, "v")
     host_dk, host_dv = pinned(dk0), pinned(dv0)
     drv = OffloadedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                            softmax_scale=s.scale, keep_activations=keep, n_buffers=nbuf, copy_cus=copy_cus)
+                            softmax_scale=s.scale, keep_activations=keep, n_buffers=nbuf, copy_cus=copy_cus,
+                            host_accumulate=host_acc)
     outs = []
     pt_d = H.dev(pt)
     drv.forward(q, k_new, v_new, host_k, host_v, pt_d,
@@ -197,9 +215,10 @@ def test_offloaded_sequence(ora, name):
 
 def test_offload_buffers_streams_and_activations_do_not_change_results():
     seed, s = SEQ["seq-qwen-shape"]
-    H.say(f"case seq-qwen-shape offloaded, 2 vs 3 staging buffers, masked vs unmasked streams: {s}")
-    _, a, outs_a, _, _, dk_a, dv_a = run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8)
-    _, b, outs_b, _, _, dk_b, dv_b = run_offloaded(s, seed, keep=True, nbuf=3, copy_cus=0)
+    H.say(f"case seq-qwen-shape offloaded: 2 vs 3 staging buffers, masked vs unmasked streams, "
+          f"host vs device gradient adds: {s}")
+    _, a, outs_a, _, _, dk_a, dv_a = run_offloaded(s, seed, keep=False, nbuf=2, copy_cus=8, host_acc=True)
+    _, b, outs_b, _, _, dk_b, dv_b = run_offloaded(s, seed, keep=True, nbuf=3, copy_cus=0, host_acc=False)
     for i in range(s.chunks):
         assert torch.equal(outs_a[i][0], outs_b[i][0]) and torch.equal(outs_a[i][1], outs_b[i][1]), f"chunk {i}"
         assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ"
