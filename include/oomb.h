@@ -152,6 +152,25 @@ int oomb_attn_bwd(const oomb_desc* desc, const void* q, const void* k_pool, cons
                   const void* dO, float* dq, float* dk_pool, float* dv_pool, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/* ---- Checking the device tables -------------------------------------------
+ * The calls above trust the contents of page_table and sel (an entry out of
+ * range is an out-of-bounds access inside a kernel).  A caller that builds
+ * them itself can check them first; this call only reads them, so any
+ * contents are safe.  counts (int32 [4], device) receives:
+ *   counts[0]  selection entries outside [0, N)
+ *   counts[1]  adjacent selection entries of a kv-head not strictly ascending
+ *   counts[2]  page-table entries (logical pages 0 .. N + C/ps - 1) outside
+ *              [0, n_slots)
+ *   counts[3]  page-table entries that repeat an earlier entry's slot (two
+ *              logical pages sharing a slot would add their gradients into
+ *              one page)
+ * All zero means the tables are valid for this descriptor.  workspace:
+ * oomb_check_workspace_bytes(desc) bytes (one counter per slot), cleared by
+ * the call itself. */
+size_t oomb_check_workspace_bytes(const oomb_desc* desc);
+int oomb_check_tables(const oomb_desc* desc, const int32_t* page_table, const int32_t* sel, int32_t* counts,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- CPU offloading of the KV cache and its gradients -------------------
  * (OOMB, section 2, "Asynchronous CPU Offloading": the KV cache and its
  * gradients, which grow with the context, live in CPU memory and move to and

@@ -60,6 +60,8 @@ def _load():
         "oomb_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_bwd_workspace_bytes": (sz, [P]),
         "oomb_attn_bwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "oomb_check_workspace_bytes": (sz, [P]),
+        "oomb_check_tables": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "oomb_host_view": (ctypes.c_int, [vp, ctypes.POINTER(vp)]),
         "oomb_stage_desc": (ctypes.c_int, [P, P]),
         "oomb_stage_tables": (ctypes.c_int, [P, vp, vp, vp]),
@@ -156,6 +158,17 @@ def oomb_attn_bwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, dO, dq, dk_p
     _check(_L.oomb_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
                             _ptr(sel), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk_pool), _ptr(dv_pool),
                             _ptr(workspace), nbytes, _stream(stream)))
+
+
+def oomb_check_workspace_bytes(desc) -> int:
+    return _L.oomb_check_workspace_bytes(ctypes.byref(desc))
+
+
+def oomb_check_tables(desc, page_table, sel, counts, workspace, workspace_bytes=None, stream=None):
+    """counts: int32 [4] device tensor (see include/oomb.h)."""
+    nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(_L.oomb_check_tables(ctypes.byref(desc), _ptr(page_table), _ptr(sel), _ptr(counts), _ptr(workspace),
+                                nbytes, _stream(stream)))
 
 
 def oomb_host_view(host) -> int:

@@ -262,6 +262,26 @@ OOMB_API int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delt
   return OOMB_OK;
 }
 
+OOMB_API size_t oomb_check_workspace_bytes(const oomb_desc* desc) {
+  oomb::Shape s;
+  if (validate(desc, &s)) return 0;
+  return (size_t)s.n_slots * 4;
+}
+
+OOMB_API int oomb_check_tables(const oomb_desc* desc, const int32_t* page_table, const int32_t* sel,
+                               int32_t* counts, void* workspace, size_t workspace_bytes, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({page_table, counts}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  if (!workspace || workspace_bytes < (size_t)s.n_slots * 4) return OOMB_ERR_WORKSPACE;
+  if (misaligned(workspace)) return OOMB_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  return launched(
+      oomb::launch_check_tables(s, page_table, sel, counts, (int32_t*)workspace, (hipStream_t)stream));
+}
+
 OOMB_API const char* oomb_status_string(int status) {
   switch (status) {
     case OOMB_OK: return "ok";

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -73,6 +75,8 @@ hipError_t launch_grad_flush(const Shape& s, float* stage_dk, float* stage_dv, f
 hipError_t launch_grads_out(const Shape& s, float* stage_dk, float* stage_dv, float* out_dk, float* out_dv,
                             hipStream_t st);
 hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st);
+hipError_t launch_check_tables(const Shape& s, const int32_t* pt, const int32_t* sel, int32_t* counts,
+                               int32_t* slot_uses, hipStream_t st);
 void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
                            const int32_t* sel, float* host_dk, float* host_dv, int n_threads);
 

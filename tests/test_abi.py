@@ -176,3 +176,16 @@ def test_stage_calls_reject_bad_arguments():
     out = P.ctypes.c_void_p()
     assert L.oomb_host_view(None, P.ctypes.byref(out)) == NULL_PTR
     assert L.oomb_host_view(A, None) == NULL_PTR
+
+
+def test_check_tables_argument_checks():
+    d = good()
+    L = P._L
+    assert P.oomb_check_workspace_bytes(d) == 4 * 2080
+    assert P.oomb_check_workspace_bytes(good(chunk_len=4000)) == 0
+    dr = P.ctypes.byref(d)
+    assert L.oomb_check_tables(dr, A, A, None, B, 4 * 2080, None) == NULL_PTR
+    assert L.oomb_check_tables(dr, A, None, A, B, 4 * 2080, None) == NULL_PTR    # K_eff > 0 needs sel
+    assert L.oomb_check_tables(dr, A, A, A, B, 4 * 2080 - 4, None) == WORKSPACE
+    assert L.oomb_check_tables(dr, A, A, A, None, 4 * 2080, None) == WORKSPACE
+    assert L.oomb_check_tables(dr, A, A, A, B + 8, 4 * 2080, None) == MISALIGNED
