@@ -108,8 +108,9 @@ def cpu_baseline(p, seed, x, tokens):
     t_rows = time.perf_counter() - t0
     t_step = t_sel + t_rows * (p.c / tokens)
     return {"value": p.c / t_step, "unit": "tokens/s", "cores": ora.threads(), "kind": "oracle",
-            "sample": (f"rep vectors of the chunk's pages and selection over the full chunk ({t_sel:.2f} s) + forward and backward (dQ, and dK/dV "
-                       f"of every key) of {tokens} of {p.c} chunk tokens x {p.hq} heads ({t_rows:.2f} s), "
+            "sample": (f"rep vectors of the chunk's pages and selection over the full chunk ({t_sel:.2f} s) + "
+                       f"forward and backward (dQ, and dK/dV of every key) of {tokens} of {p.c} chunk tokens "
+                       f"x {p.hq} heads ({t_rows:.2f} s), "
                        f"scaled to {p.c} tokens; fp64"),
             "seconds": t_sel + t_rows, "rep_setup_seconds": t_setup}
 

@@ -284,41 +284,44 @@ class OffloadedSequence:
         adds = {}
         worker = ThreadPoolExecutor(max_workers=1) if self.host_accumulate else None
 
-        with torch.cuda.stream(comp):
-            gather(last)
-            for i in reversed(range(self.n_chunks)):
-                b, a = i % self.nbuf, self._act(i)
-                sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
-                comp.wait_event(gathered[i])
-                if i + self.nbuf <= last:
-                    comp.wait_event(cleared[i + self.nbuf])  # gradient staging b is back at zero
-                if not self.keep_activations:
-                    oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], stream=comp)
-                oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
-                              self.stage_dk[b], self.stage_dv[b], self.ws_bwd, stream=comp)
-                bwd_done[i] = ev()
-                bwd_done[i].record(comp)
-                if i > 0:
-                    gather(i - 1)
-                if self.host_accumulate and i + 2 in adds:
-                    adds.pop(i + 2).result()  # delta buffer i % 2 has been added on the host
-                with torch.cuda.stream(self.d2h):  # in chunk order on one stream
-                    self.d2h.wait_event(bwd_done[i])
+        try:
+            with torch.cuda.stream(comp):
+                gather(last)
+                for i in reversed(range(self.n_chunks)):
+                    b, a = i % self.nbuf, self._act(i)
+                    sd, sel_s, pt_s, sk, sv = self._staged_call_args(i, b)
+                    comp.wait_event(gathered[i])
+                    if i + self.nbuf <= last:
+                        comp.wait_event(cleared[i + self.nbuf])  # gradient staging b is back at zero
+                    if not self.keep_activations:
+                        oomb_attn_fwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], stream=comp)
+                    oomb_attn_bwd(sd, q[i], sk, sv, pt_s, sel_s, self.o[a], self.lse[a], dO[i], self.dq[i],
+                                  self.stage_dk[b], self.stage_dv[b], self.ws_bwd, stream=comp)
+                    bwd_done[i] = ev()
+                    bwd_done[i].record(comp)
+                    if i > 0:
+                        gather(i - 1)
+                    if self.host_accumulate and i + 2 in adds:
+                        adds.pop(i + 2).result()  # delta buffer i % 2 has been added on the host
+                    with torch.cuda.stream(self.d2h):  # in chunk order on one stream
+                        self.d2h.wait_event(bwd_done[i])
+                        if self.host_accumulate:
+                            oomb_stage_grads_out(self.descs[i], self.stage_dk[b], self.stage_dv[b], *dviews[i % 2],
+                                                 stream=self.d2h)
+                        else:
+                            oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table,
+                                                   self.sel[i], hdk, hdv, stream=self.d2h)
+                        cleared[i] = ev()
+                        cleared[i].record(self.d2h)
                     if self.host_accumulate:
-                        oomb_stage_grads_out(self.descs[i], self.stage_dk[b], self.stage_dv[b], *dviews[i % 2],
-                                             stream=self.d2h)
-                    else:
-                        oomb_stage_flush_grads(self.descs[i], self.stage_dk[b], self.stage_dv[b], page_table,
-                                               self.sel[i], hdk, hdv, stream=self.d2h)
-                    cleared[i] = ev()
-                    cleared[i].record(self.d2h)
+                        adds[i] = worker.submit(accumulate, i)  # runs while the device computes chunk i-1
                 if self.host_accumulate:
-                    adds[i] = worker.submit(accumulate, i)  # runs while the device computes chunk i-1
-            if self.host_accumulate:
-                for i in sorted(adds, reverse=True):
-                    adds.pop(i).result()
-                worker.shutdown()
-            comp.wait_event(cleared[0])
+                    for i in sorted(adds, reverse=True):
+                        adds.pop(i).result()
+                comp.wait_event(cleared[0])
+        finally:
+            if worker is not None:
+                worker.shutdown(wait=True)
         self._leave(comp, caller)
         return self.dq
 

@@ -13,7 +13,8 @@ import paged_sparse_attention_amd as P
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "oomb.h")
 
-OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH, NOT_MAPPED = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
+NOT_MAPPED = -8
 A = 0x10000        # a fake, 16-byte aligned device address
 B = 0x20000
 
