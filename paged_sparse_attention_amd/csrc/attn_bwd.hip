@@ -428,7 +428,7 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   const int t_lo = div_g(g, r0);
   const int nkeys = pk + div_g(g, last_row) + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
-  PageSlots<kPageCache> pages{page_tab};
+  PageSlots<kPageCache> pages{(lds_int*)page_tab};
   pages.fill(g, a.pt, a.sel, h, (nkeys + (1 << g.ps_log2) - 1) >> g.ps_log2, tid, NT);
   __syncthreads();
 
@@ -437,22 +437,27 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   KV kv{lds_k, lds_v};
   // one page lookup per tile when the tile lies inside a page (see the forward)
   const bool tile_in_page = BN <= (1 << g.ps_log2);
-  auto load = [&](int j) {
-    if (tile_in_page) {
-      const int64_t base = pages.key_offset<D>(g, a.pt, a.sel, h, j * BN);
-      kv.load(j, kp, vp, tid, [base](int r) -> int64_t { return base + (int64_t)r * D; });
-    } else {
-      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t {
-        return pages.key_offset<D>(g, a.pt, a.sel, h, min(j * BN + r, nkeys - 1));
-      });
-    }
-  };
   const int vm_per_tile = KV::loads_per_tile(wave);
 
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) qacc[db] = zero16();
 
+  // The key loop, once per kind of page lookup (see Bool).
+  auto run = [&](auto cached_tag) {
+  constexpr bool kCached = decltype(cached_tag)::value;
+  auto offset = [&](int jj) -> int64_t {
+    if constexpr (kCached) return pages.key_offset_cached<D>(g, h, jj);
+    else return key_offset<D>(g, a.pt, a.sel, h, jj);
+  };
+  auto load = [&](int j) {
+    if (tile_in_page) {
+      const int64_t base = offset(j * BN);
+      kv.load(j, kp, vp, tid, [base](int r) -> int64_t { return base + (int64_t)r * D; });
+    } else {
+      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t { return offset(min(j * BN + r, nkeys - 1)); });
+    }
+  };
   for (int j = 0; j < KV::PD && j < ntiles; ++j) load(j);
   for (int it = 0; it < ntiles; ++it) {
     const int j0 = it * BN;
@@ -493,6 +498,9 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
       }
     }
   }
+  };
+  if (pages.cached) run(Bool<true>());
+  else run(Bool<false>());
 
   if (row_ok) {
     float* dqrow = a.dq + qoff;

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   const int t_lo = div_g(g, r0);
   const int nkeys = pk + div_g(g, last_row) + 1;  // prior keys + chunk tokens up to the block's last
   const int ntiles = (nkeys + BN - 1) / BN;
-  PageSlots<kPageCache> pages{page_tab};
+  PageSlots<kPageCache> pages{(lds_int*)page_tab};
   pages.fill(g, a.pt, a.sel, h, (nkeys + (1 << g.ps_log2) - 1) >> g.ps_log2, tid, NT);
   __syncthreads();
 
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   const int t_lo = div_g(g, r0);
   const int nkeys = pk + div_g(g, last_row) + 1;
   const int ntiles = (nkeys + BN - 1) / BN;
-  PageSlots<kPageCache> pages{page_tab};
+  PageSlots<kPageCache> pages{(lds_int*)page_tab};
   pages.fill(g, a.pt, a.sel, h, (nkeys + (1 << g.ps_log2) - 1) >> g.ps_log2, tid, NT);
   __syncthreads();
 
@@ -245,15 +245,6 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   KV kv{lds_k, lds_v};
   const bool tile_in_page = BN <= (1 << g.ps_log2);
   const typename KV::Lanes lanes = KV::lane_offsets(tid, D);
-  auto load = [&](int j) {
-    if (tile_in_page) {
-      kv.load_rows(j, kp, vp, pages.key_offset<D>(g, a.pt, a.sel, h, j * BN), lanes, tid);
-    } else {
-      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t {
-        return pages.key_offset<D>(g, a.pt, a.sel, h, min(j * BN + r, nkeys - 1));
-      });
-    }
-  };
   const int vm_per_tile = KV::loads_per_tile(wave);
 
   // S^T of tile j (keys as rows, this lane's query row as the column)
@@ -294,6 +285,20 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
 
   f32x16 scur[BN / 32], snext[BN / 32];
+  // The key loop, once per kind of page lookup (see Bool).
+  auto run = [&](auto cached_tag) {
+  constexpr bool kCached = decltype(cached_tag)::value;
+  auto offset = [&](int jj) -> int64_t {
+    if constexpr (kCached) return pages.key_offset_cached<D>(g, h, jj);
+    else return key_offset<D>(g, a.pt, a.sel, h, jj);
+  };
+  auto load = [&](int j) {
+    if (tile_in_page) {
+      kv.load_rows(j, kp, vp, offset(j * BN), lanes, tid);
+    } else {
+      kv.load(j, kp, vp, tid, [&, j](int r) -> int64_t { return offset(min(j * BN + r, nkeys - 1)); });
+    }
+  };
   for (int j = 0; j < PD && j < ntiles; ++j) load(j);
   kv.commit(0, min(PD - 1, ntiles - 1), vm_per_tile, tid);
   __syncthreads();
@@ -363,6 +368,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
       }
     }
   }
+  };
+  if (pages.cached) run(Bool<true>());
+  else run(Bool<false>());
 
   l = wave_xor_sum(l, 32);
   if (row_ok) {

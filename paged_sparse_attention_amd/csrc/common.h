@@ -133,8 +133,13 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 // Physical slots of the pages of a kv-head's key list J(h) -- the K_eff
 // selected pages, then the chunk's C/ps pages -- cached in LDS by a workgroup
 // (when they fit in CAP entries; otherwise read from global memory).
+// The table pointer is typed as LDS (address space 3): reads through a generic
+// pointer compile to flat loads, which count as vector memory operations, so
+// the wait for the slot would also wait for every tile load still in flight.
+typedef __attribute__((address_space(3))) int lds_int;
+
 template <int CAP> struct PageSlots {
-  int* tab;  // LDS, CAP entries
+  lds_int* tab;  // LDS, CAP entries
   bool cached;
 
   // all threads of the workgroup call this, then synchronise before use
@@ -148,9 +153,20 @@ template <int CAP> struct PageSlots {
   __device__ __forceinline__ int64_t key_offset(const Geo& g, const int32_t* __restrict__ pt,
                                                 const int32_t* __restrict__ sel, int h, int jj) const {
     if (!cached) return oomb::key_offset<D>(g, pt, sel, h, jj);
+    return key_offset_cached<D>(g, h, jj);
+  }
+  // the same, for a caller that has already checked `cached`
+  template <int D>
+  __device__ __forceinline__ int64_t key_offset_cached(const Geo& g, int h, int jj) const {
     const int64_t slot = tab[jj >> g.ps_log2];
     return ((slot * g.hkv + h) * (int64_t)(1 << g.ps_log2) + (jj & ((1 << g.ps_log2) - 1))) * D;
   }
+};
+// Compile-time bool for generic lambdas: a kernel runs its key loop through
+// run(Bool<true>()) or run(Bool<false>()), so each copy of the loop holds one
+// kind of page lookup only.
+template <bool B> struct Bool {
+  static constexpr bool value = B;
 };
 constexpr int kPageCache = 1024;
 
