@@ -383,6 +383,9 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ, query-major.
 // ---------------------------------------------------------------------------
+#ifndef DQ_PIPE
+#define DQ_PIPE 1
+#endif
 template <typename T> constexpr int dq_waves() { return sizeof(T) == 2 ? 8 : 4; }
 template <typename T> constexpr int dq_bm() { return 32 * dq_waves<T>(); }  // query rows per workgroup
 template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 128 : 32; }  // keys per tile
@@ -466,15 +469,19 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
     if (it + KV::PD < ntiles) load(it + KV::PD);
     const TL tk = kv.ta(it), tv = kv.tb(it);
     const bool masked = j0 + BN - 1 - pk > t_lo || j0 + BN > nkeys;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      f32x16 sacc = zero16(), pacc = zero16();
+    // S^T and dP^T of one 32-key block
+    auto sdp = [&](int kb, f32x16& sacc, f32x16& pacc) {
+      sacc = zero16();
+      pacc = zero16();
 #pragma unroll
       for (int s = 0; s < D / KS; ++s) {
         sacc = M::mma(tk.frag_rm(kb * 32 + col, s, hh), qf[s], sacc);
         pacc = M::mma(tv.frag_rm(kb * 32 + col, s, hh), df[s], pacc);
       }
-      // invisible pairs take exponent -inf (weight 0), so exp2 runs unconditionally
+    };
+    // dS^T in place of dP^T; invisible pairs take exponent -inf (weight 0),
+    // so exp2 runs unconditionally
+    auto softmax = [&](int kb, const f32x16& sacc, f32x16& pacc) {
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -490,13 +497,36 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
           pacc[e] = p * (pacc[e] - my_dt);
         }
       }
+    };
+    auto dq_mma = [&](int kb, const f32x16& pacc) {
 #pragma unroll
       for (int s = 0; s < 32 / KS; ++s) {
         const typename M::frag sf = M::pack(pacc, s * KL);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) qacc[db] = M::mma(tk.frag_tr(kb, db, s, lane), sf, qacc[db]);
       }
+    };
+#if DQ_PIPE
+    // Software-pipelined by one block: the S^T/dP^T MFMAs of block kb+1 are
+    // issued before the softmax of block kb, so the matrix core works while
+    // the VALU takes the exponentials.
+    f32x16 sacc[2], pacc[2];
+    sdp(0, sacc[0], pacc[0]);
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      if (kb + 1 < BN / 32) sdp(kb + 1, sacc[(kb + 1) & 1], pacc[(kb + 1) & 1]);
+      softmax(kb, sacc[kb & 1], pacc[kb & 1]);
+      dq_mma(kb, pacc[kb & 1]);
     }
+#else
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 sacc, pacc;
+      sdp(kb, sacc, pacc);
+      softmax(kb, sacc, pacc);
+      dq_mma(kb, pacc);
+    }
+#endif
   }
   };
   if (pages.cached) run(Bool<true>());
