@@ -157,6 +157,88 @@ def measured_traffic(kernel, workload):
     return t["traffic_bytes_per_launch"]
 
 
+def _short_kernel_name(name):
+    """liboomb kernel name out of a (mangled or demangled) symbol, else None."""
+    import re
+    m = re.search(r"oomb::(\w+)", name)
+    if m:
+        return m.group(1)
+    m = re.search(r"4oomb(\d+)(\w+)", name)
+    if m:
+        return m.group(2)[: int(m.group(1))]
+    return None
+
+
+def _counter_per_dispatch(csv_dir, counter):
+    """{kernel: [value per dispatch]} from a rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (name, _), v in sorted(per.items(), key=lambda kv: int(kv[0][1])):
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def record_traffic(dirs, kernel, workload, copy_mib, commands):
+    """Write profiles/traffic_<kernel>_<workload>.json from four rocprofv3 runs
+    (FETCH_SIZE and WRITE_SIZE of the step, then of the copy calibration) and
+    print the per-kernel table.  Counter readings are KiB per dispatch; each is
+    scaled by bytes moved / reading for the plain copy of copy_mib MiB."""
+    fetch, write, cfetch, cwrite = (_counter_per_dispatch(d, c) for d, c in
+                                    zip(dirs, ("FETCH_SIZE", "WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")))
+    copy_bytes = copy_mib << 20
+
+    def copy_reading(t):
+        vals = [v for n, vs in t.items() if "copyBuffer" in n for v in vs]
+        big = [v for v in vals if v * 1024 > copy_bytes / 8]  # the 1 GiB copies, not torch's fills
+        return sum(big) / len(big)
+
+    cf, cw = copy_reading(cfetch), copy_reading(cwrite)
+    ff, fw = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+
+    def mean_by_kernel(t):
+        out = {}
+        for n, vs in t.items():
+            k = _short_kernel_name(n)
+            if k is None:
+                continue
+            if k == "rep_update_kernel":
+                vs = vs[1:]  # the first call is the untimed set-up pass over the prior pages
+            out[k] = sum(vs) / len(vs)
+        return out
+
+    mf, mw = mean_by_kernel(fetch), mean_by_kernel(write)
+    rows = []
+    for k in mf:
+        rows.append((k, mf[k], mw.get(k, 0.0), mf[k] * 1024 * ff / 1e6, mw.get(k, 0.0) * 1024 * fw / 1e6))
+    rec = {
+        "kernel": kernel, "workload": workload, "source_sha256": source_digest(),
+        "fetch_kib_per_dispatch": mf[kernel], "write_kib_per_dispatch": mw[kernel],
+        "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_factor": ff, "write_factor": fw,
+        "traffic_bytes_per_launch": (mf[kernel] * ff + mw[kernel] * fw) * 1024,
+        "commands": commands,
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(f"wrote {path}: {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB per launch; "
+          f"factors fetch {ff:.4f}, write {fw:.4f}")
+    print("| Kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (MB) | written (MB) |")
+    print("|---|---|---|---|---|")
+    for k, a, b, r, w in rows:
+        print(f"| {k} | {a:.0f} | {b:.0f} | {r:.1f} | {w:.1f} |")
+
+
 def _time_passes(args, fwd, bwd, hip_path):
     """W untimed, then K timed forward+backward passes on the current stream.
     Returns (ms per pass by the host clock, forward ms, backward ms by events)."""
@@ -296,9 +378,22 @@ def main():
                     help="with --offload: compute units reserved for the copy kernels (0: no partition)")
     ap.add_argument("--host-accumulate", action="store_true",
                     help="with --offload: add the gradients on the host CPU instead of on the device over the link")
+    ap.add_argument("--record-traffic", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="no GPU: turn the csv output of four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of "
+                         "this benchmark, then of --copy-calibration) into profiles/traffic_<kernel>_<workload>.json")
+    ap.add_argument("--traffic-kernel", default="dkdv_kernel")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), the reference for HBM byte counters")
     args = ap.parse_args()
+    if args.record_traffic:
+        d = args.record_traffic
+        cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- python3 bench.py --copy-calibration 1024",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- python3 bench.py --copy-calibration 1024"]
+        record_traffic(d, args.traffic_kernel, args.workload, 1024, cmds)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
