@@ -128,6 +128,44 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n, "launches": 5}), flush=True)
 
 
+def measured_peaks(P):
+    """The part's sustained bf16 MFMA rate (the library's probe kernel: register
+    operands, four independent chains per wave, 4 workgroups of 4 waves per CU)
+    and its device-copy bandwidth (a 1 GiB copy, read plus write), each the best
+    of five timed launches on the current stream."""
+    import torch
+    blocks, iters = 1024, 8192  # 4 workgroups per CU: the best of a sweep of grid sizes
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    P.oomb_probe_mfma_peak(blocks, iters // 8, out)  # warm-up
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        P.oomb_probe_mfma_peak(blocks, iters, out)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    if not bool((out == 4.0 * iters).all()):
+        raise RuntimeError("MFMA probe returned a wrong check value")
+    mfma_tflops = blocks * 4 * 4 * iters * 32768 / (best / 1e3) / 1e12
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_copy_gbs": 2 * n / (best / 1e3) / 1e9}
+
+
 SOURCE_DIRS = ("paged_sparse_attention_amd/csrc", "include")
 
 
@@ -505,6 +543,12 @@ def main():
         "attention_ms": attn_ms,
         "kernels": kernels,
     }
+    if p.dtype == "bf16":
+        mp = measured_peaks(P)
+        mp["attention_mfma_frac_of_measured"] = attn_flops / (attn_ms / 1e3) / 1e12 / mp["mfma_bf16_tflops"]
+        if bound == "mfma":
+            mp["dominant_frac_of_measured"] = roof["achieved"] / mp["mfma_bf16_tflops"]
+        out["measured_peaks"] = mp
     if not args.no_cpu_baseline:
         print("bench: timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p, seed, x, args.cpu_tokens)

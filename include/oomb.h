@@ -260,6 +260,17 @@ int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delta_dk, con
                                const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
                                int32_t n_threads);
 
+/* ---- Measurement helper (not a step of the attention path) --------------
+ * Sustained bf16 MFMA rate of the device: launches n_blocks workgroups of 4
+ * waves on `stream`; every wave issues 4 * iters v_mfma_f32_32x32x16_bf16
+ * (32768 flop each) on register operands, in four independent accumulation
+ * chains, and writes one float, out[wave] = 4 * iters exactly (a check that
+ * the work ran), to out[n_blocks * 4] (device, caller-owned).  Time it with
+ * events on `stream`: flop = n_blocks * 4 * 4 * iters * 32768.  Returns
+ * OOMB_ERR_BAD_SHAPE unless 1 <= n_blocks <= 65536 and 1 <= iters <= 2^20,
+ * OOMB_ERR_NULL_PTR / OOMB_ERR_MISALIGNED for `out`, before any HIP call. */
+int oomb_probe_mfma_peak(int32_t n_blocks, int32_t iters, float* out, void* stream);
+
 /* Static text for a status code (host). */
 const char* oomb_status_string(int status);
 

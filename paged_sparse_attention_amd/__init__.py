@@ -70,6 +70,7 @@ def _load():
         "oomb_stage_flush_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_stage_grads_out": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "oomb_host_accumulate_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, i32]),
+        "oomb_probe_mfma_peak": (ctypes.c_int, [i32, i32, vp, vp]),
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "oomb_abi_version": (ctypes.c_int, []),
         "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -169,6 +170,11 @@ def oomb_check_tables(desc, page_table, sel, counts, workspace, workspace_bytes=
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     _check(_L.oomb_check_tables(ctypes.byref(desc), _ptr(page_table), _ptr(sel), _ptr(counts), _ptr(workspace),
                                 nbytes, _stream(stream)))
+
+
+def oomb_probe_mfma_peak(n_blocks, iters, out, stream=None):
+    """Measurement helper: out is a float32 device tensor of n_blocks * 4 (see include/oomb.h)."""
+    _check(_L.oomb_probe_mfma_peak(n_blocks, iters, _ptr(out), _stream(stream)))
 
 
 def oomb_host_view(host) -> int:

@@ -282,6 +282,14 @@ OOMB_API int oomb_check_tables(const oomb_desc* desc, const int32_t* page_table,
       oomb::launch_check_tables(s, page_table, sel, counts, (int32_t*)workspace, (hipStream_t)stream));
 }
 
+OOMB_API int oomb_probe_mfma_peak(int32_t n_blocks, int32_t iters, float* out, void* stream) {
+  if (n_blocks < 1 || n_blocks > 65536 || iters < 1 || iters > (1 << 20)) return OOMB_ERR_BAD_SHAPE;
+  int rc = check_ptrs({out});
+  if (rc) return rc;
+  (void)hipGetLastError();
+  return launched(oomb::launch_probe_mfma(n_blocks, iters, out, (hipStream_t)stream));
+}
+
 OOMB_API const char* oomb_status_string(int status) {
   switch (status) {
     case OOMB_OK: return "ok";

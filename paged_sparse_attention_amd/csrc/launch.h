@@ -77,6 +77,7 @@ hipError_t launch_grads_out(const Shape& s, float* stage_dk, float* stage_dv, fl
 hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_stage, hipStream_t st);
 hipError_t launch_check_tables(const Shape& s, const int32_t* pt, const int32_t* sel, int32_t* counts,
                                int32_t* slot_uses, hipStream_t st);
+hipError_t launch_probe_mfma(int n_blocks, int iters, float* out, hipStream_t st);
 void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
                            const int32_t* sel, float* host_dk, float* host_dv, int n_threads);
 

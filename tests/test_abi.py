@@ -190,3 +190,13 @@ def test_check_tables_argument_checks():
     assert L.oomb_check_tables(dr, A, A, A, B, 4 * 2080 - 4, None) == WORKSPACE
     assert L.oomb_check_tables(dr, A, A, A, None, 4 * 2080, None) == WORKSPACE
     assert L.oomb_check_tables(dr, A, A, A, B + 8, 4 * 2080, None) == MISALIGNED
+
+
+def test_probe_argument_checks():
+    L = P._L
+    assert L.oomb_probe_mfma_peak(0, 1, A, None) == BAD_SHAPE
+    assert L.oomb_probe_mfma_peak(65537, 1, A, None) == BAD_SHAPE
+    assert L.oomb_probe_mfma_peak(1, 0, A, None) == BAD_SHAPE
+    assert L.oomb_probe_mfma_peak(1, (1 << 20) + 1, A, None) == BAD_SHAPE
+    assert L.oomb_probe_mfma_peak(1, 1, None, None) == NULL_PTR
+    assert L.oomb_probe_mfma_peak(1, 1, A + 4, None) == MISALIGNED
