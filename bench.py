@@ -327,12 +327,21 @@ def sequence_bench(args):
     dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
     keep = not args.recompute
+    nbytes = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
+    m0 = torch.cuda.memory_allocated()
     drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
                           softmax_scale=s.scale, keep_activations=keep)
+    driver_bytes = torch.cuda.memory_allocated() - m0
     hip_path = P.hip_runtimes_loaded()[0]
+    torch.cuda.reset_peak_memory_stats()
     ms, fwd_ms, bwd_ms = _time_passes(args, lambda: drv.forward(q, k, v, pt),
                                       lambda: drv.backward(q, k, v, pt, do, dk, dv), hip_path)
-    resident = {"ms_per_step": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms}
+    # device memory: Q and dO of every chunk are inputs of this single-layer
+    # driver (a model makes them chunk by chunk); dQ of every chunk is its output
+    resident = {"ms_per_step": ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                "device_bytes": {"q_do_inputs": nbytes(q, do), "kv_pools": nbytes(k, v), "dkdv_pools": nbytes(dk, dv),
+                                 "driver": driver_bytes, "driver_dq_output": nbytes(drv.dq),
+                                 "peak_allocated": torch.cuda.max_memory_allocated()}}
     offload = None
     if args.offload:
         from paged_sparse_attention_amd.offload import OffloadedSequence
@@ -347,9 +356,12 @@ def sequence_bench(args):
         k_new, v_new = k[slots], v[slots]
         del k, v, dk, dv, drv
         torch.cuda.empty_cache()
+        m0 = torch.cuda.memory_allocated()
         off = OffloadedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
                                 softmax_scale=s.scale, keep_activations=keep, copy_cus=args.copy_cus,
                                 host_accumulate=args.host_accumulate)
+        off_driver_bytes = torch.cuda.memory_allocated() - m0
+        torch.cuda.reset_peak_memory_stats()
         ms, fwd_ms, bwd_ms = _time_passes(
             args, lambda: off.forward(q, k_new, v_new, host_k, host_v, pt),
             lambda: off.backward(q, do, host_k, host_v, host_dk, host_dv, pt), hip_path)
@@ -368,7 +380,10 @@ def sequence_bench(args):
                    "host_to_device_bytes_per_step": h2d, "device_to_host_bytes_per_step": d2h,
                    "host_pool_bytes": 2 * host_k.numel() * eb + 2 * host_dk.numel() * 4,
                    "device_staging_bytes": sum(t.numel() * t.element_size()
-                                               for t in off.stage_k + off.stage_v + off.stage_dk + off.stage_dv)}
+                                               for t in off.stage_k + off.stage_v + off.stage_dk + off.stage_dv),
+                   "device_bytes": {"q_do_inputs": nbytes(q, do), "new_chunk_kv_inputs": nbytes(k_new, v_new),
+                                    "driver": off_driver_bytes, "driver_dq_output": nbytes(off.dq),
+                                    "peak_allocated": torch.cuda.max_memory_allocated()}}
     del x
     tokens = s.chunks * s.c
     flops = 14.0 * s.d * s.pairs()

@@ -96,13 +96,14 @@ class OffloadedSequence:
                 oomb_stage_tables(self.descs[i], sel_s, pt_s)
                 self._tables[ke] = (sel_s, pt_s)
         # rep update of chunk i's pages reads them from staging: logical page
-        # N_i + j -> staging slot Hkv*K_eff_i + j
-        self._pt_rep = []
+        # N_i + j -> staging slot Hkv*K_eff_i + j.  The chunks' page ranges are
+        # disjoint, so one table of every page holds all of them (O(pages) of
+        # device memory, not one table per chunk).
+        self._pt_rep = torch.zeros(self.total_pages, **i32)
         for i in range(n_chunks):
-            t = torch.zeros(self.prior_pages(i) + self.chunk_pages, **i32)
             nsel = self.hkv * self.keff(i)
-            t[self.prior_pages(i):] = torch.arange(nsel, nsel + self.chunk_pages, **i32)
-            self._pt_rep.append(t)
+            self._pt_rep[self.prior_pages(i):self.prior_pages(i) + self.chunk_pages] = torch.arange(
+                nsel, nsel + self.chunk_pages, **i32)
         n_stage = max(sd.n_slots for sd in self.staged)
         blk = (n_stage, n_kv_heads, page_size, head_dim)
         self.stage_k = [torch.empty(blk, dtype=TORCH_DTYPE[dtype], device=device) for _ in range(n_buffers)]
@@ -186,7 +187,7 @@ class OffloadedSequence:
                                           stream=self.h2d)
                     if i >= 1:
                         pb = (i - 1) % self.nbuf
-                        oomb_stage_gather(self.descs[i], self.stage_k[pb], self.stage_v[pb], self._pt_rep[i - 1],
+                        oomb_stage_gather(self.descs[i], self.stage_k[pb], self.stage_v[pb], self._pt_rep,
                                           self.sel[i], OOMB_STAGE_SELECTED, self.stage_k[b], self.stage_v[b],
                                           src_slots=self.staged[i - 1].n_slots, first_page=recent,
                                           n_pages=self.chunk_pages, stream=self.h2d)
@@ -211,7 +212,7 @@ class OffloadedSequence:
                     comp.wait_event(offloaded[i - self.nbuf])  # buffer b's chunk pages are in the host pools
                 sk[nsel:nsel + self.chunk_pages].copy_(k_new[i])
                 sv[nsel:nsel + self.chunk_pages].copy_(v_new[i])
-                oomb_rep_update(self.descs[i], sk, self._pt_rep[i], self.prior_pages(i), self.chunk_pages,
+                oomb_rep_update(self.descs[i], sk, self._pt_rep, self.prior_pages(i), self.chunk_pages,
                                 self.rep, stream=comp)
                 if i + 1 < self.n_chunks and self.keff(i + 1) > 0:
                     oomb_select_topk(self.descs[i + 1], q[i + 1], self.rep, self.sel[i + 1], None, self.ws_select,
