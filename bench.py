@@ -301,6 +301,82 @@ def _time_passes(args, fwd, bwd, hip_path):
     return (t1 - t0) * 1e3 / args.steps, f, b
 
 
+def layer_bench(args):
+    """A Qwen2-style decoder layer (random weights) around the attention path,
+    forward over all chunks then backward in reverse with each chunk's forward
+    re-run (paged_sparse_attention_amd.layer); one JSON line with tokens/s, the
+    attention kernels' share of the pass and the device memory it held."""
+    import numpy as np
+    import torch
+
+    import synth
+    import paged_sparse_attention_amd as P
+    from paged_sparse_attention_amd.layer import WEIGHTS, ChunkedDecoderLayer
+
+    seed, s = synth.LAYERS[args.layer]
+    print(f"bench: layer {args.layer} {s}", file=sys.stderr, flush=True)
+    bits = synth.make_layer_inputs(s, seed)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    x, dy = dev(bits["x"]), dev(bits["dy"]).float()
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(s.pages).astype(np.int32))
+    m0 = torch.cuda.memory_allocated()
+    layer = ChunkedDecoderLayer(s.hidden, s.hq, s.hkv, s.d, s.inter, s.ps, s.c, s.chunks, s.k,
+                                {n: dev(bits[n]) for n in WEIGHTS}, page_table=perm, rope_theta=s.rope_theta,
+                                eps=s.eps)
+    del bits
+    layer_bytes = torch.cuda.memory_allocated() - m0
+    torch.cuda.reset_peak_memory_stats()
+    hip = HipEvents(P.hip_runtimes_loaded()[0], 2 * 16 * s.chunks)  # per pass: at most 16 launches a chunk
+    fwd_ms, bwd_ms, attn_ms = [], [], []
+    for it in range(args.warmup + args.steps):
+        timed = it >= args.warmup
+        if timed:
+            P.oomb_trace_events(hip.handles)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        layer.forward(x)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        layer.backward(x, dy)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        if timed:
+            n = P.oomb_trace_count()
+            if n <= 0:
+                raise RuntimeError(f"kernel tracing recorded nothing (status {n})")
+            attn_ms.append(sum(hip.elapsed_ms(2 * i, 2 * i + 1) for i in range(n)))
+            P.oomb_trace_events(None)
+            fwd_ms.append((t1 - t0) * 1e3)
+            bwd_ms.append((t2 - t1) * 1e3)
+    fwd, bwd, attn = statistics.median(fwd_ms), statistics.median(bwd_ms), statistics.median(attn_ms)
+    ms = fwd + bwd
+    tokens = s.tokens
+    qd, kd = s.hq * s.d, s.hkv * s.d
+    params = s.hidden * (qd + 2 * kd) + qd * s.hidden + 3 * s.hidden * s.inter
+    # GEMM flops of the pass: forward 2*params per token, backward 4*params
+    # per token plus the re-run forward 2*params per token
+    gemm_flops = 8.0 * params * tokens
+    cp = s.c // s.ps
+    pairs = sum(s.hq * (s.c * min(s.k, i * cp) * s.ps + s.c * (s.c + 1) // 2) for i in range(s.chunks))
+    out = {
+        "metric": "decoder layer (random weights) chunk-recurrent fwd+bwd tokens/s, attention on the paged path",
+        "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "fwd_ms": fwd, "bwd_ms": bwd, "attention_kernels_ms": attn,
+        "attention_share": attn / ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.layer, "hidden": s.hidden, "n_q_heads": s.hq, "n_kv_heads": s.hkv,
+                   "head_dim": s.d, "intermediate": s.inter, "page_size": s.ps, "chunk_len": s.c,
+                   "chunks": s.chunks, "tokens": tokens, "top_k": s.k, "seed": seed,
+                   "activations": "one chunk, forward re-run in the backward"},
+        "gemm_tflops": gemm_flops / ((ms - attn) / 1e3) / 1e12,
+        "attention_tflops": 14.0 * s.d * pairs / (attn / 1e3) / 1e12,
+        "device_bytes": {"layer": layer_bytes, "peak_allocated": torch.cuda.max_memory_allocated(),
+                         "inputs_x_dy": x.numel() * 2 + dy.numel() * 4},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def sequence_bench(args):
     """Chunk-recurrent forward (chunks in order) and backward (reverse order) of
     one layer over a whole synthetic sequence; one JSON line.  With --offload
@@ -421,6 +497,9 @@ def main():
     ap.add_argument("--sequence", default=None, metavar="NAME",
                     help="instead of one chunk step, time chunk-recurrent forward and backward over a whole "
                          "sequence (synth.SEQUENCES, e.g. seq-64k)")
+    ap.add_argument("--layer", default=None, metavar="NAME",
+                    help="instead of one chunk step, time a decoder layer with random weights around the path, "
+                         "chunk by chunk, forward and backward (synth.LAYERS, e.g. layer-qwen-64k)")
     ap.add_argument("--recompute", action="store_true",
                     help="with --sequence: keep one chunk's O/LSE and re-run each chunk's forward in the backward "
                          "(14*D flop per pair are still credited; the re-run forward is extra work)")
@@ -449,6 +528,12 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.layer:
+        if args.gpus != 1:
+            print("bench.py: one GPU only", file=sys.stderr)
+            sys.exit(2)
+        layer_bench(args)
         return
     if args.sequence:
         if args.gpus != 1:

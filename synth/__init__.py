@@ -224,3 +224,81 @@ def as_float(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return widen_bf16(a).astype(np.float64)
     return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# A decoder layer around the attention path (Qwen2-style block: RMSNorm,
+# QKV projections with bias, rotary positions, output projection, RMSNorm,
+# SwiGLU MLP).  Only its seeded inputs live here: weights, layer input and
+# output gradient, all bf16.
+# ---------------------------------------------------------------------------
+S_LAYER = 40  # stream ids S_LAYER + i for the tensors of LAYER_TENSORS
+
+
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    hidden: int
+    hq: int
+    hkv: int
+    d: int
+    inter: int
+    ps: int
+    c: int
+    chunks: int
+    k: int
+    rope_theta: float = 1.0e6
+    eps: float = 1.0e-6
+
+    @property
+    def chunk_pages(self) -> int:
+        return self.c // self.ps
+
+    @property
+    def pages(self) -> int:
+        return self.chunks * self.chunk_pages
+
+    @property
+    def tokens(self) -> int:
+        return self.chunks * self.c
+
+
+def layer_tensors(s: Layer) -> dict:
+    """name -> (shape, kind): 'w' weight N(0,1)/sqrt(fan in), 'b' bias
+    0.1*N(0,1), 'g' norm gain 1 + 0.1*N(0,1), 'x' activation N(0,1)."""
+    qd, kd = s.hq * s.d, s.hkv * s.d
+    return {
+        "ln1": ((s.hidden,), "g"), "wq": ((s.hidden, qd), "w"), "bq": ((qd,), "b"),
+        "wk": ((s.hidden, kd), "w"), "bk": ((kd,), "b"), "wv": ((s.hidden, kd), "w"), "bv": ((kd,), "b"),
+        "wo": ((qd, s.hidden), "w"), "ln2": ((s.hidden,), "g"), "wg": ((s.hidden, s.inter), "w"),
+        "wu": ((s.hidden, s.inter), "w"), "wd": ((s.inter, s.hidden), "w"),
+        "x": ((s.tokens, s.hidden), "x"), "dy": ((s.tokens, s.hidden), "x"),
+    }
+
+
+def make_layer_inputs(s: Layer, seed: int) -> dict:
+    """bf16 bits (uint16) of every weight, of the layer input x [tokens][hidden]
+    and of the output gradient dy [tokens][hidden]."""
+    out = {}
+    for i, (name, (shape, kind)) in enumerate(layer_tensors(s).items()):
+        if kind == "g":
+            g = 1.0 + 0.1 * normals(seed, S_LAYER + i, int(np.prod(shape)))
+            out[name] = bf16_bits(g.reshape(shape))
+        else:
+            scale = {"w": 1.0 / np.sqrt(shape[0]), "b": 0.1, "x": 1.0}[kind]
+            out[name] = tensor(seed, S_LAYER + i, shape, "bf16", scale)
+    return out
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float64 -> bf16 bits, round to nearest even (finite inputs)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+# name -> (seed, Layer)
+LAYERS = {
+    "layer-tiny": (11, Layer(hidden=256, hq=4, hkv=2, d=64, inter=512, ps=16, c=64, chunks=4, k=2)),
+    "layer-tiny-d128": (13, Layer(hidden=256, hq=2, hkv=1, d=128, inter=384, ps=32, c=64, chunks=5, k=3)),
+    "layer-qwen-64k": (12, Layer(hidden=3584, hq=28, hkv=4, d=128, inter=18944, ps=128, c=4096, chunks=16, k=64)),
+}

@@ -1,0 +1,82 @@
+"""The decoder layer around the paged attention (paged_sparse_attention_amd.layer)
+on the device against the fp64 reference (oracle/layer.py), through a whole
+chunk-recurrent forward and backward: the layer output, the input gradient and
+every weight gradient, with the reference attending through the device's page
+selections; and the device's selections against the reference's own.
+
+Tolerance: the device rounds to bf16 the normed activations, q/k/v, P and dS
+inside the attention, O, the MLP's gate/up/product, and (in the backward) the
+same tensors' gradients entering each bf16 GEMM.  One rounding is a relative
+error of at most 2^-9 (RMS 2^-9/sqrt(3) = 1.1e-3); about twenty of them lie
+on the longest chain from the input to a weight gradient, which bounds the
+relative RMS error near sqrt(20) * 1.1e-3 = 5e-3 when they are independent.
+The bar is 2e-2 relative RMS and a max-abs error of 5e-2 of the largest
+reference value.  The bias gradient of k has the largest relative error: it
+sums dk over the tokens, which the softmax's shift invariance nearly cancels
+(the keys' gradients of one query row sum to zero before the rotation), so
+its reference value is small.  Selections: pages whose reference scores lie within 2e-2 of
+the K-th best score, relative to the largest score, may swap (the scores are
+dot products of bf16-rounded means)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import layer as R
+from paged_sparse_attention_amd.layer import WEIGHTS, ChunkedDecoderLayer
+
+pytestmark = pytest.mark.gpu
+
+RMS_REL, MAX_REL, SEL_BAND = 2e-2, 5e-2, 2e-2
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _close(name, got, ref):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, name
+    assert np.isfinite(got).all(), name
+    err = got - ref
+    rms_rel = np.sqrt((err ** 2).mean()) / max(np.sqrt((ref ** 2).mean()), 1e-30)
+    max_rel = np.abs(err).max() / max(np.abs(ref).max(), 1e-30)
+    print(f"{name}: rms_rel {rms_rel:.2e} max_rel {max_rel:.2e}", flush=True)
+    assert rms_rel <= RMS_REL and max_rel <= MAX_REL, (name, rms_rel, max_rel)
+
+
+def _check_selection(s, gpu_sels, ref):
+    for i in range(1, s.chunks):
+        sc = ref["scores"][i]
+        for h in range(s.hkv):
+            g, r = set(gpu_sels[i][h].tolist()), set(ref["sel"][i][h].tolist())
+            if g == r:
+                continue
+            kth = np.sort(sc[h])[::-1][len(r) - 1]
+            band = SEL_BAND * np.abs(sc[h]).max()
+            for p in g ^ r:  # every swapped page lies near the K-th score
+                assert abs(sc[h][p] - kth) <= band, (i, h, p, sc[h][p], kth)
+
+
+@pytest.mark.parametrize("name", ["layer-tiny", "layer-tiny-d128"])
+def test_layer_matches_reference(name):
+    seed, s = synth.LAYERS[name]
+    bits = synth.make_layer_inputs(s, seed)
+    perm = np.random.default_rng(seed).permutation(s.pages).astype(np.int32)
+    layer = ChunkedDecoderLayer(s.hidden, s.hq, s.hkv, s.d, s.inter, s.ps, s.c, s.chunks, s.k,
+                                {n: _dev_bf16(bits[n]) for n in WEIGHTS}, page_table=torch.from_numpy(perm),
+                                rope_theta=s.rope_theta, eps=s.eps)
+    x = _dev_bf16(bits["x"])
+    dy = _dev_bf16(bits["dy"]).float()
+    y = layer.forward(x)
+    dx = layer.backward(x, dy)
+    torch.cuda.synchronize()
+    cp = s.c // s.ps
+    sels = [layer.sel[i][:, :min(s.k, i * cp)].cpu().numpy().astype(np.int64) for i in range(s.chunks)]
+    ref = R.run(s, bits, sels=sels)
+    _check_selection(s, sels, ref)
+    _close("y", y.cpu().numpy(), ref["y"])
+    _close("dx", dx.cpu().numpy(), ref["dx"])
+    for n in WEIGHTS:
+        _close("d" + n, layer.grads[n].cpu().numpy(), ref["grads"][n])
+
