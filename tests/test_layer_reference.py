@@ -6,9 +6,13 @@ Each pin checks the reference against something other than itself:
   torch's causal scaled-dot-product attention;
 - its page selection against the C attention oracle's rep -> mean query ->
   scores -> top-K chain on the same fp64 keys and queries;
-- the rotary positions against two properties of a rotation by position:
-  norms are kept, and q.k depends only on the distance of the positions;
+- the rotary positions against the closed form of one pair, (cos t, sin t),
+  and two properties of a rotation by position: norms are kept, and q.k
+  depends only on the distance of the positions;
 - RMSNorm against its defining property (unit root-mean-square).
+Planted in a copy of the reference, a flipped rotation sign, a causal mask
+with u < t, and a chunk-mean query over one head of the group each fail at
+least one of these.
 """
 import numpy as np
 import pytest
@@ -104,3 +108,13 @@ def test_layer_inputs_are_seeded_and_shaped():
         assert a[n].shape == shape and a[n].dtype == np.uint16
         assert np.array_equal(a[n], b[n])
     assert not np.array_equal(a["wq"], synth.make_layer_inputs(s, 12)["wq"])
+
+
+def test_rotary_closed_form_of_one_pair():
+    # one pair (D = 2): the frequency is 1 whatever theta, so (1, 0) at
+    # position t becomes (cos t, sin t) and (0, 1) becomes (-sin t, cos t)
+    t = torch.arange(7, dtype=torch.float64)
+    e0 = torch.tensor([1.0, 0.0], dtype=torch.float64).expand(7, 1, 2).clone()
+    e1 = torch.tensor([0.0, 1.0], dtype=torch.float64).expand(7, 1, 2).clone()
+    assert torch.allclose(R.rotary(e0, 1.0e6)[:, 0], torch.stack([t.cos(), t.sin()], -1), atol=1e-15)
+    assert torch.allclose(R.rotary(e1, 1.0e6)[:, 0], torch.stack([-t.sin(), t.cos()], -1), atol=1e-15)
