@@ -45,6 +45,8 @@ struct BwdArgs {
   float* dv;
   float* dt;       // workspace [Hq][C]: rowsum(dO * O)
   float* lse2;     // workspace [Hq][C]: lse * log2(e)
+  __bf16* bias;    // workspace [Hq][C][16]: -lse2/scale_log2, then -Dt, each as three bf16 parts that sum
+                   // to it exactly and five zeros (the dK/dV kernel's bias operands, bf16 inputs)
   float* part_k;   // workspace [splits-1][Hkv][nkeys][D], scaled dK partials of splits 1..
   float* part_v;   // workspace [splits-1][Hkv][nkeys][D]
   int splits;
@@ -57,6 +59,18 @@ struct BwdArgs {
 // a thread takes kDtRows rows, their loads issued together.
 // ---------------------------------------------------------------------------
 constexpr int kDtRows = 4;
+
+// x as three bf16 values whose sum is x exactly (8 significant bits each; x
+// normal and far from the fp32 range limits): hi = x rounded, then the
+// remainders, each exact in fp32.
+__device__ __forceinline__ void split_bf16x3(float x, __bf16* out) {
+  const __bf16 hi = (__bf16)x;
+  const float r1 = x - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  out[0] = hi;
+  out[1] = mid;
+  out[2] = (__bf16)(r1 - (float)mid);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void dt_kernel(BwdArgs a) {
@@ -92,7 +106,20 @@ __global__ __launch_bounds__(256) void dt_kernel(BwdArgs a) {
       const int t = row / a.g.hq, g = row % a.g.hq;  // row = t * Hq + g
       const int64_t i = (int64_t)g * a.g.c + t;
       a.dt[i] = s;
-      a.lse2[i] = a.lse[i] * kLog2e;
+      const float l2 = a.lse[i] * kLog2e;
+      a.lse2[i] = l2;
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 rs, rp;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rs[k] = rp[k] = (__bf16)0.f;
+        __bf16 part[3];
+        split_bf16x3(-l2 / a.scale_log2, part);
+        rs[0] = part[0], rs[1] = part[1], rs[2] = part[2];
+        split_bf16x3(-s, part);
+        rp[0] = part[0], rp[1] = part[1], rp[2] = part[2];
+        *reinterpret_cast<bf16x8*>(a.bias + i * 16) = rs;
+        *reinterpret_cast<bf16x8*>(a.bias + i * 16 + 8) = rp;
+      }
     }
   }
 }
@@ -158,8 +185,17 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   __shared__ __attribute__((aligned(16))) T lds_q[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_d[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_keys[kKeysInLds ? KeyStore<__bf16, D>::TK::ELEMS : 1];
-  __shared__ __attribute__((aligned(16))) float rlse[QD::NS][BM];  // per tile row: lse * log2(e)
-  __shared__ __attribute__((aligned(16))) float rdt[QD::NS][BM];   // per tile row: Dt
+#ifndef DKDV_BIAS
+#define DKDV_BIAS 1
+#endif
+  // bf16: each tile row's -lse2/scale_log2 and -Dt enter S and dP as the first
+  // MFMA of each chain (A = the row's three bf16 parts in k = 0..2 and zeros,
+  // B = ones), so the softmax needs no per-row operands.  Two 16-byte A
+  // fragments per row; row BM is zeros (the A operand's k = 8..15 half).
+  constexpr bool kBias = DKDV_BIAS && sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) float rlse[kBias ? 1 : QD::NS][BM];  // per tile row: lse * log2(e)
+  __shared__ __attribute__((aligned(16))) float rdt[kBias ? 1 : QD::NS][BM];   // per tile row: Dt
+  __shared__ __attribute__((aligned(16))) __bf16 rbias[kBias ? QD::NS : 1][BM + 1][16];
 
   const Geo& g = a.g;
   const KvPlan plan = kv_plan(g, KEYS);
@@ -233,11 +269,27 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
     if (!done) qd.load(j, qp, dp, tid, [=](int r) -> int64_t { return base + (int64_t)min(r, tmax) * tok_stride; });
     if (wave == 0 && lane < BM) {
       const int64_t i = (int64_t)(h * g.G + gi) * g.c + t0 + min(lane, tmax);
-      load_lds_dword(a.lse2 + i, rlse[j % QD::NS]);
-      load_lds_dword(a.dt + i, rdt[j % QD::NS]);
+      if constexpr (!kBias) {
+        load_lds_dword(a.lse2 + i, rlse[j % QD::NS]);
+        load_lds_dword(a.dt + i, rdt[j % QD::NS]);
+      }
+    }
+    if constexpr (kBias) {
+      // 32 bytes a row: lane l of a load carries half l % 2 of row l / 2
+      if (wave == 0) {
+#pragma unroll
+        for (int r0 = 0; r0 < 2 * BM; r0 += 64) {
+          const int64_t i = (int64_t)(h * g.G + gi) * g.c + t0 + min((r0 + lane) / 2, tmax);
+          __builtin_amdgcn_global_load_lds((gbl_void*)(a.bias + i * 16 + ((r0 + lane) & 1) * 8),
+                                           (lds_void*)&rbias[j % QD::NS][r0 / 2][0], 16, 0, 0);
+        }
+      }
     }
   };
-  const int vm_per_tile = QD::loads_per_tile(wave) + (wave == 0 ? 2 : 0);
+  const int vm_per_tile = QD::loads_per_tile(wave) + (wave == 0 ? (kBias ? 2 * BM / 64 : 2) : 0);
+  if constexpr (kBias) {
+    if (tid < QD::NS * 16) rbias[kBias ? tid / 16 : 0][BM][tid % 16] = (__bf16)0.f;  // visible after the first barrier
+  }
 
   // a 32-row block needs no per-element visibility test when every row is a
   // real token and every key of this wave is a valid prior key or a chunk
@@ -255,12 +307,22 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
     __syncthreads();
     if (it + QD::PD < ntiles) load(it + QD::PD);
     const TL tq = qd.ta(it), td = qd.tb(it);
-    const float* ml = rlse[it % QD::NS];
-    const float* md = rdt[it % QD::NS];
+    const float* ml = rlse[kBias ? 0 : it % QD::NS];
+    const float* md = rdt[kBias ? 0 : it % QD::NS];
     const int t0 = tile_t0(it);
 #pragma unroll 1
     for (int rb = 0; rb < BM / 32; ++rb) {
       f32x16 sacc = zero16(), pacc = zero16();
+      if constexpr (kBias) {
+        // lane (row col, half hh): its row's parts in k = 0..7 (hh = 0), the zero row (hh = 1);
+        // B is ones everywhere, which the zero half makes harmless
+        const __bf16* rec = &rbias[it % QD::NS][hh == 0 ? rb * 32 + col : BM][0];
+        typename M::frag ones;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ones[k] = (__bf16)1.f;
+        sacc = M::mma(*reinterpret_cast<const bf16x8*>(rec), ones, sacc);      // S = -lse2/scale_log2 + Q K^T
+        pacc = M::mma(*reinterpret_cast<const bf16x8*>(rec + 8), ones, pacc);  // dP = -Dt + dO V^T
+      }
 #pragma unroll
       for (int s = 0; s < D / KS; ++s) sacc = M::mma(tq.frag_rm(rb * 32 + col, s, hh), ks.frag(s, col, hh), sacc);
 #pragma unroll
@@ -273,7 +335,25 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
       const int tb = t0 + rb * 32;
       const bool full = tb + 32 <= g.c && wave_keys_ok && (wave_prior || tb >= wave_last - pk);
       // rows acc_row(4i + j, hh) = 8i + 4hh + j: four consecutive rows per i
-      if (full) {
+      if constexpr (kBias) {
+        if (full) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(sacc[e] * a.scale_log2);
+            sacc[e] = p;
+            pacc[e] = p * pacc[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int t = tb + acc_row(e, hh);
+            const bool vis = key_ok && t < g.c && my_u <= t;  // my_u < 0 for prior keys
+            const float p = __builtin_amdgcn_exp2f(vis ? sacc[e] * a.scale_log2 : -INFINITY);
+            sacc[e] = p;
+            pacc[e] = p * pacc[e];
+          }
+        }
+      } else if (full) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(ml + rb * 32 + 8 * i + 4 * hh);
@@ -556,7 +636,8 @@ BwdPlan bwd_plan(const Shape& s) {
   const size_t rowvec = (((size_t)s.hq * s.c * 4) + 255) & ~(size_t)255;
   p.off_dt = 0;
   p.off_lse2 = rowvec;
-  size_t off = 2 * rowvec;
+  p.off_bias = 2 * rowvec;
+  size_t off = 2 * rowvec + ((((size_t)s.hq * s.c * 32) + 255) & ~(size_t)255);
   p.splits = kp.splits;
   p.off_part_k = off;
   const size_t part = kp.splits > 1 ? (size_t)(kp.splits - 1) * s.hkv * nkeys * s.d * 4 : 0;
@@ -614,6 +695,7 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const v
   a.dv = dv_pool;
   a.dt = (float*)((char*)ws + p.off_dt);
   a.lse2 = (float*)((char*)ws + p.off_lse2);
+  a.bias = (__bf16*)((char*)ws + p.off_bias);
   a.part_k = (float*)((char*)ws + p.off_part_k);
   a.part_v = (float*)((char*)ws + p.off_part_v);
   a.splits = p.splits;

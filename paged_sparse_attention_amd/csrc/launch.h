@@ -45,6 +45,7 @@ SelectPlan select_plan(const Shape& s);
 struct BwdPlan {
   size_t off_dt;                  // Dt = rowsum(dO * O) per (head, token), fp32 [Hq][C]
   size_t off_lse2;                // lse * log2(e) per (head, token), fp32 [Hq][C]
+  size_t off_bias;                // dK/dV bias operands per (head, token), bf16 [Hq][C][16]
   size_t off_part_k, off_part_v;  // dK / dV partial sums of row splits 1.., fp32 [splits-1][Hkv][nkeys][D]
   int splits;                     // workgroups sharing one key block's query rows
   size_t bytes;
