@@ -15,8 +15,8 @@ Device work: the projections, norms, rotary positions and the MLP are torch
 operations on bf16 tensors (library GEMMs, fp32 accumulation); every step of
 the attention runs in liboomb's kernels: the chunk's pages into the pools, rep
 update, top-K selection, fused forward, fused backward with dK/dV added into
-the pools.  Weights are kept as fp32 masters and cast to bf16 per use, so their
-gradients accumulate over the chunks in fp32.
+the pools.  Weights are kept as fp32 masters and cast to bf16 once per sweep;
+each chunk's weight gradients are added into fp32 sums.
 
 Per chunk i (positions i*C .. i*C + C - 1):
   forward   h = rms(x) * ln1; q, k, v = h W + b; rotary(q, k); k, v -> pages
@@ -171,24 +171,25 @@ class ChunkedDecoderLayer:
 
     def backward(self, x, dy):
         """Chunks in reverse with their saved selections.  Returns dx fp32; the
-        weight gradients are left in grads (fp32 masters' shapes)."""
+        weight gradients are left in grads (fp32, the masters' shapes).  The
+        bf16 weights are cast once for the sweep and are the autograd leaves;
+        each chunk's weight gradients (bf16, as the GEMMs give them) are added
+        into fp32 sums and cleared."""
         self.dk_pool.zero_()
         self.dv_pool.zero_()
-        for t in self.master.values():
-            t.requires_grad_(True)
-            t.grad = None
+        w = {n: t.to(torch.bfloat16).requires_grad_(True) for n, t in self.master.items()}
+        self.grads = {n: torch.zeros_like(t) for n, t in self.master.items()}
         dx = torch.empty((self.n_chunks * self.c, self.h), dtype=torch.float32, device=x.device)
         for i in reversed(range(self.n_chunks)):
             xi = x[i * self.c:(i + 1) * self.c].detach().float().requires_grad_(True)
             with torch.enable_grad():
-                w = self._weights()
                 xb = xi.to(torch.bfloat16)
                 q, k, v = self._qkv(xb, i, w)
                 o = _PagedAttention.apply(q, k, v, self, i)
                 y = self._mlp_block(xi, o, w)
                 torch.autograd.backward(y, dy[i * self.c:(i + 1) * self.c])
             dx[i * self.c:(i + 1) * self.c] = xi.grad
-        self.grads = {n: t.grad for n, t in self.master.items()}
-        for t in self.master.values():
-            t.requires_grad_(False)
+            for n, t in w.items():
+                self.grads[n].add_(t.grad)
+                t.grad = None
         return dx
