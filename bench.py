@@ -542,7 +542,7 @@ def main():
         sequence_bench(args)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards by kv-head across GPUs by design but no multi-GPU code is built", file=sys.stderr)
         sys.exit(2)
 
