@@ -260,6 +260,45 @@ int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delta_dk, con
                                const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
                                int32_t n_threads);
 
+/* ---- The decoder block around the attention (not steps of the method) ---
+ * Qwen2-style block pieces, so that a layer around the path runs chunk by
+ * chunk without chains of small framework kernels: RMSNorm, rotary positions
+ * (rotate-half pairing), SwiGLU, forward and backward.  All device pointers,
+ * row-major, asynchronous on `stream`; fp32 accumulation, bf16 outputs rounded
+ * once (RNE).  Host checks run before any HIP call: OOMB_ERR_NULL_PTR,
+ * OOMB_ERR_BAD_SHAPE, OOMB_ERR_MISALIGNED (fp32 row buffers 16-byte aligned,
+ * bf16 buffers 8-byte aligned), OOMB_ERR_BAD_DTYPE.
+ *
+ * oomb_rmsnorm_fwd: h[r][:] = x[r][:] * rstd[r] * gain, with rstd[r] =
+ *   1/sqrt(mean(x[r][:]^2) + eps).  x fp32 [rows][hidden], gain bf16
+ *   [hidden], h bf16 [rows][hidden], rstd fp32 [rows] (out).  hidden % 4 == 0,
+ *   hidden <= 8192.
+ * oomb_rmsnorm_bwd: dx = rstd*gain*dh - x*rstd^3*mean(gain*dh*x) (+ dres if
+ *   not NULL), per row.  dh bf16, dres/dx fp32 [rows][hidden]; rstd from the
+ *   forward.
+ * oomb_rmsnorm_gain_grad: partial[s][j] = sum over the rows r of segment s of
+ *   dh[r][j]*x[r][j]*rstd[r]; the gain gradient is the sum over s of
+ *   partial[s][:] (fp32 [segments][hidden], out).  Rows are split into
+ *   `segments` equal contiguous ranges.
+ * oomb_rotary: out = in with pair (j, j + D/2) of each head of token r turned
+ *   by the angle of position first_position + r: cos_table/sin_table fp32
+ *   [positions][D/2]; inverse != 0 turns the other way (the transpose, for
+ *   gradients).  in [rows][heads][D] of in_dtype (OOMB_F32 or OOMB_BF16), out
+ *   bf16 of the same shape (not aliasing in).
+ * oomb_swiglu_fwd: out = silu(gate) * up, bf16, n elements (n % 4 == 0).
+ * oomb_swiglu_bwd: dgate = dout*up*silu'(gate), dup = dout*silu(gate), bf16. */
+int oomb_rmsnorm_fwd(const float* x, const void* gain, int32_t rows, int32_t hidden, float eps, void* h, float* rstd,
+                     void* stream);
+int oomb_rmsnorm_bwd(const float* x, const void* gain, const float* rstd, const void* dh, const float* dres,
+                     int32_t rows, int32_t hidden, float* dx, void* stream);
+int oomb_rmsnorm_gain_grad(const float* x, const float* rstd, const void* dh, int32_t rows, int32_t hidden,
+                           int32_t segments, float* partial, void* stream);
+int oomb_rotary(const void* in, int32_t in_dtype, void* out, const float* cos_table, const float* sin_table,
+                int32_t rows, int32_t heads, int32_t head_dim, int32_t first_position, int32_t inverse, void* stream);
+int oomb_swiglu_fwd(const void* gate, const void* up, void* out, int64_t n, void* stream);
+int oomb_swiglu_bwd(const void* gate, const void* up, const void* dout, void* dgate, void* dup, int64_t n,
+                    void* stream);
+
 /* ---- Measurement helper (not a step of the attention path) --------------
  * Sustained bf16 MFMA rate of the device: launches n_blocks workgroups of 4
  * waves on `stream`; every wave issues 4 * iters v_mfma_f32_32x32x16_bf16

@@ -71,6 +71,12 @@ def _load():
         "oomb_stage_grads_out": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "oomb_host_accumulate_grads": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, i32]),
         "oomb_probe_mfma_peak": (ctypes.c_int, [i32, i32, vp, vp]),
+        "oomb_rmsnorm_fwd": (ctypes.c_int, [vp, vp, i32, i32, ctypes.c_float, vp, vp, vp]),
+        "oomb_rmsnorm_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, i32, i32, vp, vp]),
+        "oomb_rmsnorm_gain_grad": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, vp, vp]),
+        "oomb_rotary": (ctypes.c_int, [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "oomb_swiglu_fwd": (ctypes.c_int, [vp, vp, vp, ctypes.c_int64, vp]),
+        "oomb_swiglu_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, ctypes.c_int64, vp]),
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "oomb_abi_version": (ctypes.c_int, []),
         "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
@@ -175,6 +181,42 @@ def oomb_check_tables(desc, page_table, sel, counts, workspace, workspace_bytes=
 def oomb_probe_mfma_peak(n_blocks, iters, out, stream=None):
     """Measurement helper: out is a float32 device tensor of n_blocks * 4 (see include/oomb.h)."""
     _check(_L.oomb_probe_mfma_peak(n_blocks, iters, _ptr(out), _stream(stream)))
+
+
+def oomb_rmsnorm_fwd(x, gain, eps, h, rstd, stream=None):
+    """x fp32 [rows][hidden], gain bf16 [hidden] -> h bf16, rstd fp32 [rows]."""
+    rows, hidden = x.shape
+    _check(_L.oomb_rmsnorm_fwd(_ptr(x), _ptr(gain), rows, hidden, eps, _ptr(h), _ptr(rstd), _stream(stream)))
+
+
+def oomb_rmsnorm_bwd(x, gain, rstd, dh, dres, dx, stream=None):
+    rows, hidden = x.shape
+    _check(_L.oomb_rmsnorm_bwd(_ptr(x), _ptr(gain), _ptr(rstd), _ptr(dh), _ptr(dres), rows, hidden, _ptr(dx),
+                               _stream(stream)))
+
+
+def oomb_rmsnorm_gain_grad(x, rstd, dh, partial, stream=None):
+    """partial: fp32 [segments][hidden]."""
+    rows, hidden = x.shape
+    _check(_L.oomb_rmsnorm_gain_grad(_ptr(x), _ptr(rstd), _ptr(dh), rows, hidden, partial.shape[0], _ptr(partial),
+                                     _stream(stream)))
+
+
+def oomb_rotary(x, out, cos_table, sin_table, first_position, inverse=False, stream=None):
+    """x fp32 or bf16 [rows][heads][D] -> out bf16 of the same shape."""
+    rows, heads, d = x.shape
+    dt = 0 if x.dtype == torch.float32 else 1
+    _check(_L.oomb_rotary(_ptr(x), dt, _ptr(out), _ptr(cos_table), _ptr(sin_table), rows, heads, d, first_position,
+                          1 if inverse else 0, _stream(stream)))
+
+
+def oomb_swiglu_fwd(gate, up, out, stream=None):
+    _check(_L.oomb_swiglu_fwd(_ptr(gate), _ptr(up), _ptr(out), gate.numel(), _stream(stream)))
+
+
+def oomb_swiglu_bwd(gate, up, dout, dgate, dup, stream=None):
+    _check(_L.oomb_swiglu_bwd(_ptr(gate), _ptr(up), _ptr(dout), _ptr(dgate), _ptr(dup), gate.numel(),
+                              _stream(stream)))
 
 
 def oomb_host_view(host) -> int:

@@ -11,9 +11,10 @@ Qwen2-style decoder block (RMSNorm, QKV projections with bias, rotary
 positions, output projection, RMSNorm, SwiGLU MLP, two residual adds) with
 random weights of a given shape; there are no trained weights or data here.
 
-Device work: the projections, norms, rotary positions and the MLP are torch
-operations on bf16 tensors (library GEMMs, fp32 accumulation); every step of
-the attention runs in liboomb's kernels: the chunk's pages into the pools, rep
+Device work: the projections are library GEMMs on bf16 tensors (fp32
+accumulation) and the residual adds are torch operations; the RMSNorms, rotary
+positions and the SwiGLU product are liboomb's fused kernels (forward and
+backward), and every step of the attention runs in liboomb's kernels: rep
 update, top-K selection, fused forward, fused backward with dK/dV added into
 the pools.  Weights are kept as fp32 masters and cast to bf16 once per sweep;
 each chunk's weight gradients are added into fp32 sums.
@@ -31,47 +32,79 @@ The residual stream y, the gradients dx and the weight gradients are fp32.
 from __future__ import annotations
 
 import torch
-import torch.nn.functional as F
 
 from . import (make_desc, oomb_attn_bwd, oomb_attn_fwd, oomb_bwd_workspace_bytes, oomb_rep_update,
-               oomb_select_topk, oomb_select_workspace_bytes)
+               oomb_rmsnorm_bwd, oomb_rmsnorm_fwd, oomb_rmsnorm_gain_grad, oomb_rotary, oomb_select_topk,
+               oomb_select_workspace_bytes, oomb_swiglu_bwd, oomb_swiglu_fwd)
 
 WEIGHTS = ("ln1", "wq", "bq", "wk", "bk", "wv", "bv", "wo", "ln2", "wg", "wu", "wd")
 
 
-def _rms(x, gain, eps):
-    x = x.float()
-    return x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + eps) * gain.float()
+class _RMSNorm(torch.autograd.Function):
+    """h = x * rstd * gain (bf16) of fp32 rows x; the library's fused kernels."""
+
+    @staticmethod
+    def forward(ctx, x, gain, eps):
+        x = x.contiguous()
+        h = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+        rstd = torch.empty(x.shape[0], dtype=torch.float32, device=x.device)
+        oomb_rmsnorm_fwd(x, gain, eps, h, rstd)
+        ctx.save_for_backward(x, gain, rstd)
+        return h
+
+    @staticmethod
+    def backward(ctx, dh):
+        x, gain, rstd = ctx.saved_tensors
+        dh = dh.to(torch.bfloat16).contiguous()
+        dx = torch.empty_like(x)
+        oomb_rmsnorm_bwd(x, gain, rstd, dh, None, dx)
+        partial = torch.empty((max(1, min(64, x.shape[0])), x.shape[1]), dtype=torch.float32, device=x.device)
+        oomb_rmsnorm_gain_grad(x, rstd, dh, partial)
+        return dx, partial.sum(dim=0), None
 
 
-def _rotary(x, cos, sin):
-    """x [C][heads][D] fp32; rotate-half pairing (i, i + D/2)."""
-    half = x.shape[-1] // 2
-    x1, x2 = x[..., :half], x[..., half:]
-    c, s = cos[:, None, :], sin[:, None, :]
-    return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
+class _SwiGLU(torch.autograd.Function):
+    """silu(gate) * up, bf16; the library's fused kernels."""
+
+    @staticmethod
+    def forward(ctx, gate, up):
+        gate, up = gate.contiguous(), up.contiguous()
+        out = torch.empty_like(gate)
+        oomb_swiglu_fwd(gate, up, out)
+        ctx.save_for_backward(gate, up)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        gate, up = ctx.saved_tensors
+        dg, du = torch.empty_like(gate), torch.empty_like(up)
+        oomb_swiglu_bwd(gate, up, dout.to(torch.bfloat16).contiguous(), dg, du)
+        return dg, du
 
 
 class _PagedAttention(torch.autograd.Function):
     """o = paged top-K chunk attention of chunk i with its saved selection, on
-    q rounded to bf16.  The pools already hold the chunk's keys and values
-    (written, rounded to bf16, in the forward sweep); k and v are inputs only
-    so that autograd routes their gradients, which the backward reads out of
-    the gradient pools.  q, k, v and their gradients are fp32."""
+    the rotary-positioned q.  q and k come in before their rotary positions
+    (bf16); the pools already hold the chunk's positioned keys and values
+    (written in the forward sweep), so k and v are inputs only so that
+    autograd routes their gradients: the backward reads them out of the
+    gradient pools and turns dq and dk back through the rotation."""
 
     @staticmethod
-    def forward(ctx, q, k, v, layer, i):
-        qb = q.to(torch.bfloat16).contiguous()
-        o, lse = layer._attend(i, qb)
-        ctx.save_for_backward(qb, o, lse)
+    def forward(ctx, q_pre, k_pre, v, layer, i):
+        q = layer._rotate(q_pre, i)
+        o, lse = layer._attend(i, q)
+        ctx.save_for_backward(q, o, lse)
         ctx.layer, ctx.i = layer, i
         return o
 
     @staticmethod
     def backward(ctx, do):
-        qb, o, lse = ctx.saved_tensors
-        dq, dk, dv = ctx.layer._attend_backward(ctx.i, qb, o, lse, do.to(torch.bfloat16).contiguous())
-        return dq, dk, dv, None, None
+        q, o, lse = ctx.saved_tensors
+        layer, i = ctx.layer, ctx.i
+        dq, dk, dv = layer._attend_backward(i, q, o, lse, do.to(torch.bfloat16).contiguous())
+        return layer._rotate(dq, i, inverse=True), layer._rotate(dk, i, inverse=True), dv.to(torch.bfloat16), \
+            None, None
 
 
 class ChunkedDecoderLayer:
@@ -117,20 +150,25 @@ class ChunkedDecoderLayer:
     def _slots(self, i):
         return self.pt[i * self.cp:(i + 1) * self.cp].long()
 
+    def _rotate(self, x, i, inverse=False):
+        """bf16 copy of x [C][heads][D] (fp32 or bf16) turned to the positions of chunk i."""
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+        oomb_rotary(x.contiguous(), out, self.cos, self.sin, i * self.c, inverse)
+        return out
+
     def _qkv(self, x, i, w):
-        """fp32 q [C][Hq][D] and k, v [C][Hkv][D] after the rotary positions."""
+        """bf16 q [C][Hq][D] and k, v [C][Hkv][D], before the rotary positions; x fp32."""
         c, hq, hkv, d = self.c, self.hq, self.hkv, self.d
-        h = _rms(x, w["ln1"], self.eps).to(torch.bfloat16)
+        h = _RMSNorm.apply(x, w["ln1"], self.eps)
         q = (h @ w["wq"] + w["bq"]).view(c, hq, d)
         k = (h @ w["wk"] + w["bk"]).view(c, hkv, d)
         v = (h @ w["wv"] + w["bv"]).view(c, hkv, d)
-        cos, sin = self.cos[i * c:(i + 1) * c], self.sin[i * c:(i + 1) * c]
-        return _rotary(q.float(), cos, sin), _rotary(k.float(), cos, sin), v.float()
+        return q, k, v
 
     def _mlp_block(self, x, o, w):
-        x1 = x.float() + (o.reshape(self.c, self.hq * self.d) @ w["wo"]).float()
-        h2 = _rms(x1, w["ln2"], self.eps).to(torch.bfloat16)
-        m = (F.silu(h2 @ w["wg"]) * (h2 @ w["wu"])) @ w["wd"]
+        x1 = x + (o.reshape(self.c, self.hq * self.d) @ w["wo"]).float()
+        h2 = _RMSNorm.apply(x1, w["ln2"], self.eps)
+        m = _SwiGLU.apply(h2 @ w["wg"], h2 @ w["wu"]) @ w["wd"]
         return x1 + m.float()
 
     def _weights(self):
@@ -157,8 +195,9 @@ class ChunkedDecoderLayer:
         w = self._weights()
         y = torch.empty((self.n_chunks * self.c, self.h), dtype=torch.float32, device=x.device)
         for i in range(self.n_chunks):
-            xi = x[i * self.c:(i + 1) * self.c]
-            q, k, v = (t.to(torch.bfloat16) for t in self._qkv(xi, i, w))
+            xi = x[i * self.c:(i + 1) * self.c].float()
+            q_pre, k_pre, v = self._qkv(xi, i, w)
+            q, k = self._rotate(q_pre, i), self._rotate(k_pre, i)
             s = self._slots(i)
             self.k_pool[s] = k.view(self.cp, self.ps, self.hkv, self.d).permute(0, 2, 1, 3)
             self.v_pool[s] = v.view(self.cp, self.ps, self.hkv, self.d).permute(0, 2, 1, 3)
@@ -183,9 +222,8 @@ class ChunkedDecoderLayer:
         for i in reversed(range(self.n_chunks)):
             xi = x[i * self.c:(i + 1) * self.c].detach().float().requires_grad_(True)
             with torch.enable_grad():
-                xb = xi.to(torch.bfloat16)
-                q, k, v = self._qkv(xb, i, w)
-                o = _PagedAttention.apply(q, k, v, self, i)
+                q_pre, k_pre, v = self._qkv(xi, i, w)
+                o = _PagedAttention.apply(q_pre, k_pre, v, self, i)
                 y = self._mlp_block(xi, o, w)
                 torch.autograd.backward(y, dy[i * self.c:(i + 1) * self.c])
             dx[i * self.c:(i + 1) * self.c] = xi.grad

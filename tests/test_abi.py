@@ -200,3 +200,19 @@ def test_probe_argument_checks():
     assert L.oomb_probe_mfma_peak(1, (1 << 20) + 1, A, None) == BAD_SHAPE
     assert L.oomb_probe_mfma_peak(1, 1, None, None) == NULL_PTR
     assert L.oomb_probe_mfma_peak(1, 1, A + 4, None) == MISALIGNED
+
+
+def test_layer_op_argument_checks():
+    L = P._L
+    assert L.oomb_rmsnorm_fwd(None, A, 4, 256, 1e-6, B, A, None) == NULL_PTR
+    assert L.oomb_rmsnorm_fwd(A, A, 4, 254, 1e-6, B, A, None) == BAD_SHAPE
+    assert L.oomb_rmsnorm_fwd(A, A, 4, 8196, 1e-6, B, A, None) == BAD_SHAPE
+    assert L.oomb_rmsnorm_fwd(A + 4, A, 4, 256, 1e-6, B, A, None) == MISALIGNED
+    assert L.oomb_rmsnorm_bwd(A, A, A, A, None, 4, 256, None, None) == NULL_PTR
+    assert L.oomb_rmsnorm_bwd(A, A, A, A, A + 8, 4, 256, B, None) == MISALIGNED
+    assert L.oomb_rmsnorm_gain_grad(A, A, A, 4, 256, 0, B, None) == BAD_SHAPE
+    assert L.oomb_rotary(A, 2, B, A, A, 4, 2, 64, 0, 0, None) == BAD_DTYPE
+    assert L.oomb_rotary(A, 1, B, A, A, 4, 2, 63, 0, 0, None) == BAD_SHAPE
+    assert L.oomb_rotary(A, 1, None, A, A, 4, 2, 64, 0, 0, None) == NULL_PTR
+    assert L.oomb_swiglu_fwd(A, A, B, 6, None) == BAD_SHAPE
+    assert L.oomb_swiglu_bwd(A, A, A, B, B + 2, 8, None) == MISALIGNED
