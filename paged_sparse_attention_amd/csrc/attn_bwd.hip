@@ -185,14 +185,11 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   __shared__ __attribute__((aligned(16))) T lds_q[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_d[QD::NS * TL::ELEMS];
   __shared__ __attribute__((aligned(16))) T lds_keys[kKeysInLds ? KeyStore<__bf16, D>::TK::ELEMS : 1];
-#ifndef DKDV_BIAS
-#define DKDV_BIAS 1
-#endif
   // bf16: each tile row's -lse2/scale_log2 and -Dt enter S and dP as the first
   // MFMA of each chain (A = the row's three bf16 parts in k = 0..2 and zeros,
   // B = ones), so the softmax needs no per-row operands.  Two 16-byte A
   // fragments per row; row BM is zeros (the A operand's k = 8..15 half).
-  constexpr bool kBias = DKDV_BIAS && sizeof(T) == 2;
+  constexpr bool kBias = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) float rlse[kBias ? 1 : QD::NS][BM];  // per tile row: lse * log2(e)
   __shared__ __attribute__((aligned(16))) float rdt[kBias ? 1 : QD::NS][BM];   // per tile row: Dt
   __shared__ __attribute__((aligned(16))) __bf16 rbias[kBias ? QD::NS : 1][BM + 1][16];
@@ -463,9 +460,6 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ, query-major.
 // ---------------------------------------------------------------------------
-#ifndef DQ_PIPE
-#define DQ_PIPE 1
-#endif
 template <typename T> constexpr int dq_waves() { return sizeof(T) == 2 ? 8 : 4; }
 template <typename T> constexpr int dq_bm() { return 32 * dq_waves<T>(); }  // query rows per workgroup
 template <typename T> constexpr int dq_bn() { return sizeof(T) == 2 ? 128 : 32; }  // keys per tile
@@ -586,7 +580,6 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
         for (int db = 0; db < D / 32; ++db) qacc[db] = M::mma(tk.frag_tr(kb, db, s, lane), sf, qacc[db]);
       }
     };
-#if DQ_PIPE
     // Software-pipelined by one block: the S^T/dP^T MFMAs of block kb+1 are
     // issued before the softmax of block kb, so the matrix core works while
     // the VALU takes the exponentials.
@@ -598,15 +591,6 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
       softmax(kb, sacc[kb & 1], pacc[kb & 1]);
       dq_mma(kb, pacc[kb & 1]);
     }
-#else
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) {
-      f32x16 sacc, pacc;
-      sdp(kb, sacc, pacc);
-      softmax(kb, sacc, pacc);
-      dq_mma(kb, pacc);
-    }
-#endif
   }
   };
   if (pages.cached) run(Bool<true>());
