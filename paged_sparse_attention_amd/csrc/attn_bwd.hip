@@ -144,8 +144,12 @@ __host__ __device__ inline KvPlan kv_plan(const Geo& g, int keys_per_wg) {
   const int nkeys = (g.keff << g.ps_log2) + g.c;
   p.nkb = (nkeys + keys_per_wg - 1) / keys_per_wg;
   const int items = p.nkb * g.hkv;
-  int s = (1536 + items - 1) / items;  // about three rounds of two workgroups per CU
-  p.splits = s < 1 ? 1 : (s > 8 ? 8 : s);
+  // at least three rounds of two workgroups per CU, and never fewer than four
+  // row shares: measured on the long-context steps (256K to 4M tokens of
+  // context, and 32K dense), four shares beat two, three and five to eight,
+  // the extra partial sums costing less than the balance they buy
+  int s = (1536 + items - 1) / items;
+  p.splits = s < 4 ? 4 : (s > 8 ? 8 : s);
   return p;
 }
 
