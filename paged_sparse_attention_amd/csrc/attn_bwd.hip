@@ -483,9 +483,9 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
   const int nrb = (rows_total + BM - 1) / BM;
-  const int item = xcd_remap(blockIdx.x, nrb * g.hkv);
-  const int h = item / nrb;
-  const int r0 = (nrb - 1 - item % nrb) * BM;  // later (heavier) row blocks first
+  const RowItem it = row_item(blockIdx.x, nrb, g.hkv);
+  const int h = it.h;
+  const int r0 = (nrb - 1 - it.rank) * BM;  // later (heavier) row blocks first
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;

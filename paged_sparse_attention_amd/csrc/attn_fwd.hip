@@ -56,9 +56,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_kernel(FwdArgs a) {
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
   const int nrb = (rows_total + kFwdBM - 1) / kFwdBM;
-  const int item = xcd_remap(blockIdx.x, nrb * g.hkv);
-  const int h = item / nrb;
-  const int r0 = (nrb - 1 - item % nrb) * kFwdBM;  // later (heavier) row blocks first
+  const RowItem it = row_item(blockIdx.x, nrb, g.hkv);
+  const int h = it.h;
+  const int r0 = (nrb - 1 - it.rank) * kFwdBM;  // later (heavier) row blocks first
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;
@@ -215,9 +215,9 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
   const int nrb = (rows_total + kFwdBM - 1) / kFwdBM;
-  const int item = xcd_remap(blockIdx.x, nrb * g.hkv);
-  const int h = item / nrb;
-  const int r0 = (nrb - 1 - item % nrb) * kFwdBM;  // later (heavier) row blocks first
+  const RowItem it = row_item(blockIdx.x, nrb, g.hkv);
+  const int h = it.h;
+  const int r0 = (nrb - 1 - it.rank) * kFwdBM;  // later (heavier) row blocks first
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, hh = lane >> 5;

@@ -130,6 +130,27 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
   return (b % 8) * per + b / 8;
 }
 
+// Row-block items of the query-major kernels (forward, dQ): nrb row blocks per
+// kv-head, ranked heaviest first (rank 0 = the last block, which sees the most
+// chunk keys).  Contiguous ranges per XCD would give one XCD a head's heavy
+// half and the next its light half, and the heavy XCD would finish last.
+// When the heads divide evenly over the XCDs (S = 8 / hkv of them per head,
+// nrb a multiple of S), the S XCDs of a head take its ranks in turn (the
+// head's s-th XCD gets ranks s, s + S, s + 2S, ...): equal shares of heavy and
+// light blocks, heaviest first on each, and still one head's pages per XCD.
+// Otherwise each XCD gets a contiguous range of items.
+struct RowItem {
+  int h, rank;
+};
+__device__ __forceinline__ RowItem row_item(int b, int nrb, int hkv) {
+  if (hkv <= 8 && 8 % hkv == 0 && nrb % (8 / hkv) == 0) {
+    const int S = 8 / hkv, x = b % 8;
+    return {x / S, (b / 8) * S + x % S};
+  }
+  const int item = xcd_remap(b, nrb * hkv);
+  return {item / nrb, item % nrb};
+}
+
 // Physical slots of the pages of a kv-head's key list J(h) -- the K_eff
 // selected pages, then the chunk's C/ps pages -- cached in LDS by a workgroup
 // (when they fit in CAP entries; otherwise read from global memory).
