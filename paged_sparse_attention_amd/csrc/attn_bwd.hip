@@ -16,10 +16,12 @@
 //      row-major LDS tiles).  When the rows are split over several workgroups
 //      for load balance, the first split adds into the pools in place and the
 //      others write partial sums to the workspace.
-//   3. kv_reduce_kernel (only with a row split): dk_pool/dv_pool += the sum of
-//      the other splits' partials, in split order.
-//   4. dq_kernel:   query-major, like the forward: S^T and dP^T per 32-key
-//      block of a K/V tile, dQ^T += K^T dS^T, written once per row.
+//   3. dq_kernel:   query-major, like the forward: S^T and dP^T per 32-key
+//      block of a K/V tile, dQ^T += K^T dS^T, written once per row.  With a
+//      row split, trailing workgroups of the same launch then add the other
+//      splits' partials into dk_pool/dv_pool, in split order: they are
+//      dispatched after every row block and fill the CUs that the last round
+//      of row blocks leaves idle.
 // Every (slot, kv-head, row) of the gradient pools is changed by exactly one
 // thread, once, in a fixed order: no atomics, bitwise reproducible, and slots
 // outside the selected and chunk pages are never touched.  P and dS are
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 
   if (!key_ok) return;
   const float sc = g.scale;
-  if (sp == 0) {  // the first split adds straight into the pools; kv_reduce adds the rest after it
+  if (sp == 0) {  // the first split adds straight into the pools; the split reduction adds the rest after it
     float* dkp = a.dk + koff;
     float* dvp = a.dv + koff;
 #pragma unroll
@@ -435,14 +437,13 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 }
 
 // dk_pool / dv_pool += sum of the partials of splits 1 .. splits-1, in split
-// order (split 0 has already added its share in place).
+// order (split 0 has already added its share in place); float4 group i of the
+// [Hkv][keys][D] key list.  Runs after dkdv_kernel has finished (a later
+// launch on the same stream).
 template <int D>
-__global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
+__device__ __forceinline__ void kv_reduce_group(const BwdArgs& a, int64_t i) {
   const Geo& g = a.g;
   const int nkeys = (g.keff << g.ps_log2) + g.c;
-  const int64_t total = (int64_t)g.hkv * nkeys * (D / 4);
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
   const int d = (int)(i % (D / 4)) * 4;
   const int64_t hk = i / (D / 4);
   const int h = (int)(hk / nkeys), jj = (int)(hk % nkeys);
@@ -459,6 +460,10 @@ __global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
   f32x4 ov = *reinterpret_cast<f32x4*>(a.dv + dst);
   *reinterpret_cast<f32x4*>(a.dk + dst) = ok + sk;
   *reinterpret_cast<f32x4*>(a.dv + dst) = ov + sv;
+}
+
+__host__ __device__ inline int64_t kv_reduce_groups(const Geo& g, int d) {
+  return (int64_t)g.hkv * ((g.keff << g.ps_log2) + g.c) * (d / 4);
 }
 
 // ---------------------------------------------------------------------------
@@ -483,6 +488,11 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   const Geo& g = a.g;
   const int rows_total = g.c * g.G;
   const int nrb = (rows_total + BM - 1) / BM;
+  if ((int)blockIdx.x >= nrb * g.hkv) {  // a trailing workgroup: NT float4 groups of the split reduction
+    const int64_t i = (int64_t)(blockIdx.x - nrb * g.hkv) * NT + threadIdx.x;
+    if (i < kv_reduce_groups(g, D)) kv_reduce_group<D>(a, i);
+    return;
+  }
   const RowItem it = row_item(blockIdx.x, nrb, g.hkv);
   const int h = it.h;
   const int r0 = (nrb - 1 - it.rank) * BM;  // later (heavier) row blocks first
@@ -650,17 +660,13 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
     Traced tr(st, "dkdv_kernel");
     hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(kp.nkb * kp.splits * a.g.hkv), dim3(kv_waves<T>() * 64), 0, st, a);
   }
-  if (kp.splits > 1) {
-    const int64_t nkeys = (a.g.keff << a.g.ps_log2) + a.g.c;
-    const int64_t total = a.g.hkv * nkeys * (D / 4);
-    Traced tr(st, "kv_reduce_kernel");
-    hipLaunchKernelGGL((kv_reduce_kernel<D>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st, a);
-  }
   const int qrows = a.g.c * a.g.G;
   {
+    constexpr int NT = dq_waves<T>() * 64;
+    const int64_t n_red = kp.splits > 1 ? (kv_reduce_groups(a.g, D) + NT - 1) / NT : 0;
     Traced tr(st, "dq_kernel");
-    hipLaunchKernelGGL((dq_kernel<T, D>), dim3(((qrows + dq_bm<T>() - 1) / dq_bm<T>()) * a.g.hkv),
-                       dim3(dq_waves<T>() * 64), 0, st, a);
+    hipLaunchKernelGGL((dq_kernel<T, D>), dim3((unsigned)(((qrows + dq_bm<T>() - 1) / dq_bm<T>()) * a.g.hkv + n_red)),
+                       dim3(NT), 0, st, a);
   }
   return hipGetLastError();
 }
