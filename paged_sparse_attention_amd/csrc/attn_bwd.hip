@@ -202,12 +202,39 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 
   const Geo& g = a.g;
   const KvPlan plan = kv_plan(g, KEYS);
-  const int item = xcd_remap(blockIdx.x, plan.nkb * plan.splits * g.hkv);
-  const int h = item / (plan.nkb * plan.splits);
-  // key blocks vary fastest: the workgroups that run together on one XCD
-  // stream the same share of query rows, which then stays in its L2
-  const int kblk = item % plan.nkb;
-  const int sp = (item / plan.nkb) % plan.splits;
+  // Work items are (row-share group = kv-head and split, key block).  Each
+  // XCD takes whole groups, so the workgroups that run together on it stream
+  // the same shares of query rows through its L2.  Within an XCD the key
+  // blocks that hold prior keys (every row sees them: the heaviest, all alike)
+  // go first, group by group, then the chunk's key blocks, which fewer rows
+  // see, heaviest first with the groups alternating: the light ones end the
+  // kernel.  Shapes whose items do not split evenly into whole groups per XCD
+  // take contiguous ranges of items per XCD instead.
+  int h, sp, kblk;
+  {
+    const int total = plan.nkb * plan.splits * g.hkv, per = total / 8;
+    const int nprior = min(plan.nkb, ((g.keff << g.ps_log2) + KEYS - 1) / KEYS);
+    if (total % 8 == 0 && per % plan.nkb == 0 && nprior > 0 && nprior < plan.nkb) {
+      const int x = blockIdx.x % 8, j = blockIdx.x / 8, gpx = per / plan.nkb;
+      int grp;
+      if (j < gpx * nprior) {
+        grp = j / nprior;
+        kblk = j % nprior;
+      } else {
+        const int jl = j - gpx * nprior;
+        grp = jl % gpx;
+        kblk = nprior + jl / gpx;
+      }
+      const int gi = x * gpx + grp;
+      h = gi / plan.splits;
+      sp = gi % plan.splits;
+    } else {
+      const int item = xcd_remap(blockIdx.x, total);
+      h = item / (plan.nkb * plan.splits);
+      kblk = item % plan.nkb;
+      sp = (item / plan.nkb) % plan.splits;
+    }
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
