@@ -38,6 +38,12 @@ SMALL = {
     "ps32-d128": (35, Problem(hq=8, hkv=2, d=128, ps=32, c=96, n=20, k=7)),
     "k-one-below-n": (36, Problem(hq=4, hkv=2, d=64, ps=16, c=32, n=9, k=8)),
     "scale-override-bf16": (37, Problem(hq=6, hkv=3, d=128, ps=128, c=128, n=5, k=2, scale=0.2)),
+    # work orders over the XCDs: one XCD per kv-head (8 kv-heads), with 8 row
+    # splits of dK/dV, so 8 row-share groups per XCD
+    "kv8-xcd-per-head": (38, Problem(hq=16, hkv=8, d=128, ps=32, c=256, n=24, k=5)),
+    # two XCDs per kv-head taking its 6 row blocks in turn, and 4 dK/dV
+    # row-share groups per XCD
+    "xcd-pairs-g3": (39, Problem(hq=12, hkv=4, d=128, ps=64, c=512, n=30, k=6)),
 }
 
 FULL = ["dense-32k", "sparse-256k", "sparse-1m", "sparse-4m"]
