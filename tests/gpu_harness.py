@@ -64,8 +64,14 @@ def touched_mask(p, ora, pt, sel):
     return m
 
 
-def run_full(p, seed, ora, report=None):
-    """Every output against the oracle, element by element (small problems)."""
+def run_full(p, seed, ora, report=None, rel_limits=None):
+    """Every output against the oracle, element by element (small problems).
+    rel_limits: {output name: r} replaces the official max-abs bar of that
+    output by r * max |reference| (a documented known limit only)."""
+    rel_limits = rel_limits or {}
+
+    def bar(name, want):
+        return rel_limits[name] * float(np.max(np.abs(want))) if name in rel_limits else None
     report = {} if report is None else report
     x = synth.make_inputs(p, seed)
     d = Device(p, x, canary_seed=seed)
@@ -101,14 +107,14 @@ def run_full(p, seed, ora, report=None):
     compare_lse(lse, ol, p.dtype, report)
 
     odq, odk, odv = ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, x["do"])
-    compare("dQ", st.dq.cpu().numpy().reshape(-1, p.d), odq, p.dtype, report)
+    compare("dQ", st.dq.cpu().numpy().reshape(-1, p.d), odq, p.dtype, report, max_abs=bar("dQ", odq))
     dk = d.dk.cpu().numpy()
     dv = d.dv.cpu().numpy()
     slot, row = ora.key_slots(p, x["page_table"], sel)
     gdk = np.stack([(dk[slot[h], h, row[h]].astype(np.float64) - d.dk0[slot[h], h, row[h]]) for h in range(p.hkv)])
     gdv = np.stack([(dv[slot[h], h, row[h]].astype(np.float64) - d.dv0[slot[h], h, row[h]]) for h in range(p.hkv)])
-    compare("dK", gdk, odk, p.dtype, report)
-    compare("dV", gdv, odv, p.dtype, report)
+    compare("dK", gdk, odk, p.dtype, report, max_abs=bar("dK", odk))
+    compare("dV", gdv, odv, p.dtype, report, max_abs=bar("dV", odv))
     untouched = ~touched_mask(p, ora, x["page_table"], sel)
     for name, after, before in (("dK", dk, d.dk0), ("dV", dv, d.dv0)):
         a = after[untouched]
@@ -128,11 +134,68 @@ def sample_rows(p, rng, n_extra=12):
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
-def run_sampled(p, seed, ora, report=None, n_local=32):
-    """Full-size problem: rep and selection exactly; O/LSE/dQ on sampled rows;
-    dK/dV of the last n_local chunk tokens (only later rows see them); softmax
-    invariants; then a second backward whose dO is zero outside the sampled rows,
-    which makes dK/dV of every key exact from those rows alone."""
+def sum_dk_model(p, x, o_gpu, check, o_ref, lse_ref, slot, row, sample):
+    """Error model of the per-kv-head sum over keys of the GPU's dK increments.
+
+    Exactly, sum_j dS_rj = 0 for every row r (softmax shift invariance), so the
+    keys' dK sum to zero.  Two roundings on the GPU leave a remainder:
+    - Dt_r = dO_r . O_r is taken from the stored O, rounded to the input type
+      (R15), while the backward's P_rj V_j sum to the unrounded O_r: each row's
+      dS then sums to e_r = dO_r . (O_r - O_gpu,r), and the keys' dK gain
+      scale * sum_r e_r Q_r over the rows r of the head's group.
+    - each dS_rj is rounded to bf16 before its MFMA: round to nearest with 8
+      significant bits leaves an error of mean zero and variance at most
+      2^-16 dS_rj^2 / 3, so component d gains a term of standard deviation at
+      most scale * sqrt(2^-16/3 * sum_r Q_rd^2 * sum_j dS_rj^2).
+    With the oracle's O on every row (check == all rows) the first term is
+    computed exactly (pred); otherwise it is taken as noise of variance
+    scale^2 * mean(e_r^2) * sum_r Q_rd^2 (pred = 0).  sum_j dS_rj^2 and e_r^2
+    are averaged over the rows `sample` (a subset of `check`), in fp64 from the
+    oracle's LSE and O.  fp32 accumulation adds far less.  o_gpu: [C*Hq][D];
+    o_ref, lse_ref: oracle values of the rows `check`; slot, row: the pool
+    position of each key of J(h).  Returns (pred, sigma), each [Hkv][D]."""
+    G = p.group
+    scale = p.scale if p.scale else 1.0 / np.sqrt(p.d)
+    do = synth.as_float(x["do"], p.dtype).reshape(p.c, p.hq, p.d)
+    q = synth.as_float(x["q"], p.dtype).reshape(p.c, p.hq, p.d)
+    pos = {int(r): i for i, r in enumerate(check)}
+    every = len(check) == p.c * p.hq
+    pk = p.keff * p.ps
+    pred = np.zeros((p.hkv, p.d))
+    sigma = np.zeros((p.hkv, p.d))
+    if every:
+        e = np.einsum("tgd,tgd->tg", do, (o_ref - o_gpu).reshape(p.c, p.hq, p.d))
+    for h in range(p.hkv):
+        sl = slice(h * G, (h + 1) * G)
+        qq = np.sum(q[:, sl] ** 2, axis=(0, 1))
+        kh = synth.as_float(x["k_pool"][slot[h], h, row[h]], p.dtype)
+        vh = synth.as_float(x["v_pool"][slot[h], h, row[h]], p.dtype)
+        ds2, e2 = [], []
+        for r in sample:
+            t, g = divmod(int(r), p.hq)
+            if g // G != h:
+                continue
+            i = pos[int(r)]
+            n = pk + t + 1                                    # prior keys, then chunk tokens u <= t
+            pr = np.exp(scale * (kh[:n] @ q[t, g]) - lse_ref[i])
+            dpr = vh[:n] @ do[t, g]
+            ds2.append(np.sum((pr * (dpr - do[t, g] @ o_ref[i])) ** 2))
+            e2.append(float(do[t, g] @ (o_ref[i] - o_gpu[r])) ** 2)
+        var = (2.0 ** -16 if p.dtype == "bf16" else 2.0 ** -48) / 3 * float(np.mean(ds2)) * qq
+        if every:
+            pred[h] = scale * np.einsum("tg,tgd->d", e[:, sl], q[:, sl])
+        else:
+            var = var + float(np.mean(e2)) * qq
+        sigma[h] = scale * np.sqrt(var)
+    return pred, sigma
+
+
+def run_sampled(p, seed, ora, report=None, n_local=32, every_row=False):
+    """Full-size problem: rep and selection exactly; O/LSE/dQ on sampled rows
+    (every row with every_row=True); dK/dV of the last n_local chunk tokens
+    (only later rows see them); softmax invariants; then a second backward
+    whose dO is zero outside the sampled rows, which makes dK/dV of every key
+    exact from those rows alone."""
     report = {} if report is None else report
     rng = np.random.default_rng(seed)
     say(f"  generating inputs {p}")
@@ -163,20 +226,24 @@ def run_sampled(p, seed, ora, report=None, n_local=32):
     report["sel_exact"] = check_selection(sel, oscores, keff)
 
     rows = sample_rows(p, rng)
-    say(f"  oracle: forward and dQ on {len(rows)} rows")
-    oo, ol = ora.fwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, rows=rows)
-    o = host(st.o).reshape(-1, p.d)[rows]
-    lse = st.lse.cpu().numpy().T.reshape(-1)[rows]
-    compare("O[rows]", o, oo, p.dtype, report)
+    check = ora.all_rows(p) if every_row else rows
+    tag = "all rows" if every_row else "rows"
+    say(f"  oracle: forward and dQ on {len(check)} rows")
+    oo, ol = ora.fwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, rows=check)
+    o_gpu = host(st.o).reshape(-1, p.d)
+    lse = st.lse.cpu().numpy().T.reshape(-1)[check]
+    compare(f"O[{tag}]", o_gpu[check], oo, p.dtype, report)
     compare_lse(lse, ol, p.dtype, report)
-    odq, _, _ = ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, x["do"], rows=rows, dkdv=False)
-    compare("dQ[rows]", st.dq.cpu().numpy().reshape(-1, p.d)[rows], odq, p.dtype, report)
+    odq, _, _ = ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, x["do"], rows=check, dkdv=False)
+    compare(f"dQ[{tag}]", st.dq.cpu().numpy().reshape(-1, p.d)[check], odq, p.dtype, report)
+    slot, row = ora.key_slots(p, x["page_table"], sel)
+    model = sum_dk_model(p, x, o_gpu, check, oo, ol, slot, row, rows)
+    del oo, ol, odq
 
     # last chunk tokens: seen only by rows t >= C - n_local
     say(f"  oracle: dK/dV of the last {n_local} chunk tokens")
     late = np.arange((p.c - n_local) * p.hq, p.c * p.hq, dtype=np.int64)
     _, odk, odv = ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, x["do"], rows=late)
-    slot, row = ora.key_slots(p, x["page_table"], sel)
     jj = np.arange(keff * p.ps + p.c - n_local, keff * p.ps + p.c)
     dk = torch.stack([d.dk[torch.from_numpy(slot[h, jj]).cuda(), h, torch.from_numpy(row[h, jj]).cuda()]
                       for h in range(p.hkv)]).double().cpu().numpy() - 0.5
@@ -189,17 +256,26 @@ def run_sampled(p, seed, ora, report=None, n_local=32):
     touched = torch.from_numpy(touched_mask(p, ora, x["page_table"], sel)).cuda()
     G = p.group
     do_sum = torch.from_numpy(synth.as_float(x["do"], p.dtype).reshape(p.c, p.hkv, G, p.d).sum(axis=(0, 2)))
-    inv_k, inv_v = 0.0, 0.0
+    inv_v = 0.0
+    sum_dk = np.zeros((p.hkv, p.d))
     for h in range(p.hkv):
         m = touched[:, h]
-        sk = (d.dk[m, h].double() - 0.5).sum(dim=(0, 1)).cpu()
+        sum_dk[h] = (d.dk[m, h].double() - 0.5).sum(dim=(0, 1)).cpu().numpy()
         sv = (d.dv[m, h].double() + 0.25).sum(dim=(0, 1)).cpu()
-        inv_k = max(inv_k, float(sk.abs().max()))
         inv_v = max(inv_v, float((sv - do_sum[h]).abs().max()))
         assert bool((d.dk[~m, h] == 0.5).all()) and bool((d.dv[~m, h] == -0.25).all()), "untouched slot changed"
+    inv_k = float(np.abs(sum_dk).max())
     report["sum_dK"] = inv_k
     report["sum_dV_minus_sum_dO"] = inv_v
-    assert inv_k <= 5e-2, f"sum of dK over keys {inv_k:.3e}"
+    # the error model: what the Dt term leaves, within 5 standard deviations
+    # of the rounding terms, component by component
+    pred, sigma = model
+    resid = sum_dk - pred
+    report["sum_dK_model"] = dict(
+        pred_max=float(np.abs(pred).max()), resid_max=float(np.abs(resid).max()),
+        resid_rms=float(np.sqrt(np.mean(resid ** 2))), sigma_mean=float(np.mean(sigma)),
+        resid_over_sigma_max=float(np.max(np.abs(resid) / sigma)))
+    assert np.all(np.abs(resid) <= 5 * sigma), f"sum of dK: residual {report['sum_dK_model']}"
     assert inv_v <= 1e-3 * float(do_sum.abs().max()), f"sum of dV - sum of dO {inv_v:.3e}"
 
     # backward again with dO zero outside the sampled rows: every key is exact from them

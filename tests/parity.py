@@ -1,16 +1,16 @@
 """Comparison rules between the HIP path and the fp64 oracle.
 
-Official bar (per element, max-abs): O, dQ, dK, dV within 2e-2 for bf16 inputs
-and 1e-4 for fp32 inputs, times max(1, max |reference|) so that cases whose
-outputs exceed 1 are held to the same relative precision; selected pages
-identical except inside the near-tie band (K-th and (K+1)-th oracle scores
-closer than 1e-4 relative).
-Stricter internal bars, so that a localised bug cannot hide under an absolute
-bound close to the outputs' own RMS: rms(err) / rms(ref) <= 1e-2 (bf16) or
-1e-5 (fp32), and |LSE err| <= 2e-4 (bf16) or 1e-5 (fp32).  The bf16 bound
-follows from the arithmetic: S and dP are exact products of bf16 inputs summed
-in fp32; P and dS are rounded once to bf16 (relative 2^-9 ~ 2e-3) before
-their MFMAs, so relative RMS errors of a few 1e-3 are expected.
+Official bar (per element, max-abs, absolute): O, dQ, dK, dV within 2e-2 for
+bf16 inputs and 1e-4 for fp32 inputs; selected pages identical except inside
+the near-tie band (K-th and (K+1)-th oracle scores closer than 1e-4 relative).
+
+Internal bars, named separately from the official one, so that a localised bug
+cannot hide under an absolute bound close to the outputs' own RMS:
+rms(err) / rms(ref) <= 1e-2 (bf16) or 1e-5 (fp32), and |LSE err| <= 2e-4
+(bf16) or 1e-5 (fp32).  The bf16 bound follows from the arithmetic: S and dP
+are exact products of bf16 inputs summed in fp32; P and dS are rounded once to
+bf16 (8 significant bits: relative error at most 2^-8 ~ 3.9e-3, about 2^-8/sqrt(3)
+rms) before their MFMAs, so relative RMS errors of a few 1e-3 are expected.
 """
 from __future__ import annotations
 
@@ -22,7 +22,10 @@ LSE_ABS = {"bf16": 2e-4, "f32": 1e-5}
 TIE_REL = 1e-4
 
 
-def compare(name, got, want, dtype, report=None):
+def compare(name, got, want, dtype, report=None, max_abs=None):
+    """Official max-abs bar, plus the internal rms bar.  `max_abs` replaces the
+    official bar only for a documented known limit (see
+    test_gpu_parity.test_bf16_large_scale_known_limit)."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (name, got.shape, want.shape)
@@ -35,12 +38,9 @@ def compare(name, got, want, dtype, report=None):
     rms_rel = float(np.sqrt(np.mean(err ** 2))) / max(rms_ref, 1e-30)
     if report is not None:
         report[name] = dict(max_abs=max_err, rms_rel=rms_rel, rms_ref=rms_ref)
-    # The official bound is absolute, set for outputs of magnitude below 1 (every
-    # benchmark configuration).  Rounding P and dS to the input type is a relative
-    # error, so for larger outputs (e.g. a larger softmax scale) the bound grows
-    # with the largest reference value.
-    bound = MAX_ABS[dtype] * max(1.0, float(np.max(np.abs(want))))
-    assert max_err <= bound, f"{name}: max |err| {max_err:.3e} > {bound:.2e}"
+    if max_abs is None:
+        max_abs = MAX_ABS[dtype]
+    assert max_err <= max_abs, f"{name}: max |err| {max_err:.3e} > {max_abs:.2e}"
     if rms_ref > 0:
         assert rms_rel <= RMS_REL[dtype], f"{name}: rms rel err {rms_rel:.3e} > {RMS_REL[dtype]:.0e}"
 
