@@ -84,6 +84,24 @@ class HipEvents:
                 self.rt.hipEventDestroy(ctypes.c_void_p(h))
 
 
+def host_cpu():
+    """CPU model and logical CPU counts of this host (the oracle's machine)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": usable, "host_logical_cpus": os.cpu_count()}
+
+
 def cpu_baseline(p, seed, x, tokens):
     """The fp64 oracle, as it stands, on the host cores: the selection over the
     whole chunk plus forward and backward of `tokens` chunk tokens (all heads),
@@ -107,7 +125,7 @@ def cpu_baseline(p, seed, x, tokens):
     ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], pt, sel, x["do"], rows=rows)
     t_rows = time.perf_counter() - t0
     t_step = t_sel + t_rows * (p.c / tokens)
-    return {"value": p.c / t_step, "unit": "tokens/s", "cores": ora.threads(), "kind": "oracle",
+    return {"value": p.c / t_step, "unit": "tokens/s", "cores": ora.threads(), **host_cpu(), "kind": "oracle",
             "sample": (f"rep vectors of the chunk's pages and selection over the full chunk ({t_sel:.2f} s) + "
                        f"forward and backward (dQ, and dK/dV of every key) of {tokens} of {p.c} chunk tokens "
                        f"x {p.hq} heads ({t_rows:.2f} s), "

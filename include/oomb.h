@@ -119,7 +119,9 @@ size_t oomb_select_workspace_bytes(const oomb_desc* desc);
  *   sel[h]    = the K_eff pages of highest score, exact ties to the lower page,
  *               written in ascending page order; top_k >= N gives 0..N-1.
  * scores_out (fp32 [Hkv][N]) receives the scores when not NULL.
- * Deterministic: no atomics; repeated calls give identical bits. */
+ * Deterministic: the only atomics are integer adds into LDS histograms (their
+ * order cannot change a count), and every floating-point sum has a fixed
+ * order, so repeated calls give identical bits. */
 int oomb_select_topk(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
                      float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -255,7 +257,11 @@ int oomb_stage_grads_out(const oomb_desc* desc, float* stage_dk, float* stage_dv
  * that b stands for: page_table[sel[h][k]] or page_table[N + j].  page_table
  * and sel are HOST arrays.  Entries out of range are skipped.  Runs on
  * n_threads host threads (0 or 1: the calling thread only); each element gets
- * one fp32 add, so the result equals oomb_stage_flush_grads'. */
+ * one fp32 add, so the result equals oomb_stage_flush_grads'.  If a helper
+ * thread cannot be started, the calling thread adds that share itself: the
+ * result is the same, and no exception leaves the call.
+ * OOMB_ERR_NULL_PTR, OOMB_ERR_BAD_SHAPE (n_threads outside 0..256) from the
+ * checks; otherwise OOMB_OK. */
 int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delta_dk, const float* delta_dv,
                                const int32_t* page_table, const int32_t* sel, float* host_dk, float* host_dv,
                                int32_t n_threads);

@@ -114,6 +114,28 @@ def _ptr(x):
     raise TypeError(f"expected a tensor, an int address or None, got {type(x)}")
 
 
+_IO_DTYPE = {0: torch.float32, 1: torch.bfloat16}   # oomb_dtype -> torch dtype of q, pools, o, dO
+
+
+def _dev(x, dtype=None, name="argument"):
+    """Address of a device buffer for the C ABI.  A tensor must be on the GPU,
+    contiguous and (when given) of `dtype`, else ValueError: a host pointer, a
+    strided view or a wrong element type would reach the kernels as a bad
+    address or misread data.  An int passes through as an address, None as
+    NULL (the library's own checks then apply)."""
+    if x is None or isinstance(x, int):
+        return x
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a tensor, an int address or None, got {type(x)}")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor, got one on {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{name}: dtype {x.dtype}, expected {dtype}")
+    return x.data_ptr()
+
+
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -136,8 +158,9 @@ def oomb_abi_version() -> int:
 
 
 def oomb_rep_update(desc, k_pool, page_table, first_page, n_pages, rep, stream=None):
-    _check(_L.oomb_rep_update(ctypes.byref(desc), _ptr(k_pool), _ptr(page_table), first_page, n_pages,
-                              _ptr(rep), _stream(stream)))
+    io = _IO_DTYPE.get(desc.dtype)
+    _check(_L.oomb_rep_update(ctypes.byref(desc), _dev(k_pool, io, "k_pool"), _dev(page_table, torch.int32, "page_table"),
+                              first_page, n_pages, _dev(rep, torch.float32, "rep"), _stream(stream)))
 
 
 def oomb_select_workspace_bytes(desc) -> int:
@@ -146,13 +169,17 @@ def oomb_select_workspace_bytes(desc) -> int:
 
 def oomb_select_topk(desc, q, rep, sel, scores_out, workspace, workspace_bytes=None, stream=None):
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    _check(_L.oomb_select_topk(ctypes.byref(desc), _ptr(q), _ptr(rep), _ptr(sel), _ptr(scores_out),
-                               _ptr(workspace), nbytes, _stream(stream)))
+    io = _IO_DTYPE.get(desc.dtype)
+    _check(_L.oomb_select_topk(ctypes.byref(desc), _dev(q, io, "q"), _dev(rep, torch.float32, "rep"),
+                               _dev(sel, torch.int32, "sel"), _dev(scores_out, torch.float32, "scores_out"),
+                               _dev(workspace, None, "workspace"), nbytes, _stream(stream)))
 
 
 def oomb_attn_fwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, stream=None):
-    _check(_L.oomb_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-                            _ptr(sel), _ptr(o), _ptr(lse), _stream(stream)))
+    io = _IO_DTYPE.get(desc.dtype)
+    _check(_L.oomb_attn_fwd(ctypes.byref(desc), _dev(q, io, "q"), _dev(k_pool, io, "k_pool"), _dev(v_pool, io, "v_pool"),
+                            _dev(page_table, torch.int32, "page_table"), _dev(sel, torch.int32, "sel"),
+                            _dev(o, io, "o"), _dev(lse, torch.float32, "lse"), _stream(stream)))
 
 
 def oomb_bwd_workspace_bytes(desc) -> int:
@@ -162,9 +189,13 @@ def oomb_bwd_workspace_bytes(desc) -> int:
 def oomb_attn_bwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, dO, dq, dk_pool, dv_pool, workspace,
                   workspace_bytes=None, stream=None):
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    _check(_L.oomb_attn_bwd(ctypes.byref(desc), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(page_table),
-                            _ptr(sel), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk_pool), _ptr(dv_pool),
-                            _ptr(workspace), nbytes, _stream(stream)))
+    io = _IO_DTYPE.get(desc.dtype)
+    f32, i32 = torch.float32, torch.int32
+    _check(_L.oomb_attn_bwd(ctypes.byref(desc), _dev(q, io, "q"), _dev(k_pool, io, "k_pool"), _dev(v_pool, io, "v_pool"),
+                            _dev(page_table, i32, "page_table"), _dev(sel, i32, "sel"), _dev(o, io, "o"),
+                            _dev(lse, f32, "lse"), _dev(dO, io, "dO"), _dev(dq, f32, "dq"),
+                            _dev(dk_pool, f32, "dk_pool"), _dev(dv_pool, f32, "dv_pool"),
+                            _dev(workspace, None, "workspace"), nbytes, _stream(stream)))
 
 
 def oomb_check_workspace_bytes(desc) -> int:
@@ -174,8 +205,10 @@ def oomb_check_workspace_bytes(desc) -> int:
 def oomb_check_tables(desc, page_table, sel, counts, workspace, workspace_bytes=None, stream=None):
     """counts: int32 [4] device tensor (see include/oomb.h)."""
     nbytes = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
-    _check(_L.oomb_check_tables(ctypes.byref(desc), _ptr(page_table), _ptr(sel), _ptr(counts), _ptr(workspace),
-                                nbytes, _stream(stream)))
+    i32 = torch.int32
+    _check(_L.oomb_check_tables(ctypes.byref(desc), _dev(page_table, i32, "page_table"), _dev(sel, i32, "sel"),
+                                _dev(counts, i32, "counts"), _dev(workspace, None, "workspace"), nbytes,
+                                _stream(stream)))
 
 
 def oomb_probe_mfma_peak(n_blocks, iters, out, stream=None):

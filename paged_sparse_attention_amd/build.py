@@ -21,7 +21,7 @@ FLAGS = [
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(out: str = LIB, extra=None, verbose: bool = False) -> str:

@@ -24,47 +24,7 @@ namespace {
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
-int log2_exact(int v) {
-  for (int b = 0; b < 31; ++b)
-    if (v == (1 << b)) return b;
-  return -1;
-}
-
-int validate(const oomb_desc* d, oomb::Shape* s) {
-  if (!d) return OOMB_ERR_NULL_PTR;
-  if (d->dtype != OOMB_F32 && d->dtype != OOMB_BF16) return OOMB_ERR_BAD_DTYPE;
-  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads != 0) return OOMB_ERR_BAD_SHAPE;
-  if (d->head_dim <= 0 || d->page_size <= 0 || d->chunk_len <= 0) return OOMB_ERR_BAD_SHAPE;
-  if (d->n_prior_pages < 0 || d->top_k < 0 || d->n_slots <= 0 || d->rep_capacity < 0) return OOMB_ERR_BAD_SHAPE;
-  if (d->chunk_len % d->page_size != 0) return OOMB_ERR_BAD_SHAPE;
-  if (!(d->softmax_scale >= 0.f) || !isfinite(d->softmax_scale)) return OOMB_ERR_BAD_SHAPE;
-  const int64_t pages_total = (int64_t)d->n_prior_pages + d->chunk_len / d->page_size;
-  if (d->n_slots < pages_total || d->rep_capacity < pages_total) return OOMB_ERR_BAD_SHAPE;
-  if (d->head_dim != 64 && d->head_dim != 128) return OOMB_ERR_UNSUPPORTED;
-  const int ps_log2 = log2_exact(d->page_size);
-  if (ps_log2 < 4 || ps_log2 > 7) return OOMB_ERR_UNSUPPORTED;
-  if ((int64_t)d->n_kv_heads * d->head_dim > 1024) return OOMB_ERR_UNSUPPORTED;
-  const int64_t G = d->n_q_heads / d->n_kv_heads;
-  if (G >= 1024) return OOMB_ERR_UNSUPPORTED;
-  const int64_t keff = d->top_k < d->n_prior_pages ? d->top_k : d->n_prior_pages;
-  // 32-bit row and key indices inside the kernels
-  if ((int64_t)d->chunk_len * G >= (1ll << 24)) return OOMB_ERR_UNSUPPORTED;
-  if (keff * d->page_size + d->chunk_len >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
-  if ((int64_t)d->chunk_len * d->n_q_heads >= (1ll << 30)) return OOMB_ERR_UNSUPPORTED;
-  s->hq = d->n_q_heads;
-  s->hkv = d->n_kv_heads;
-  s->d = d->head_dim;
-  s->ps = d->page_size;
-  s->ps_log2 = ps_log2;
-  s->c = d->chunk_len;
-  s->n = d->n_prior_pages;
-  s->keff = (int)keff;
-  s->n_slots = d->n_slots;
-  s->rep_cap = d->rep_capacity;
-  s->bf16 = d->dtype == OOMB_BF16;
-  s->scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
-  return OOMB_OK;
-}
+int validate(const oomb_desc* d, oomb::Shape* s) { return oomb::validate_desc(d, s); }
 
 // Every pointer non-NULL and 16-byte aligned.
 int check_ptrs(std::initializer_list<const void*> ps) {
@@ -258,8 +218,7 @@ OOMB_API int oomb_host_accumulate_grads(const oomb_desc* desc, const float* delt
   if (!delta_dk || !delta_dv || !page_table || !host_dk || !host_dv) return OOMB_ERR_NULL_PTR;
   if (s.keff > 0 && !sel) return OOMB_ERR_NULL_PTR;
   if (n_threads < 0 || n_threads > 256) return OOMB_ERR_BAD_SHAPE;
-  oomb::host_accumulate_grads(s, delta_dk, delta_dv, page_table, sel, host_dk, host_dv, n_threads);
-  return OOMB_OK;
+  return oomb::host_accumulate_grads(s, delta_dk, delta_dv, page_table, sel, host_dk, host_dv, n_threads);
 }
 
 OOMB_API size_t oomb_check_workspace_bytes(const oomb_desc* desc) {

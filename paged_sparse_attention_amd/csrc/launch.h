@@ -9,15 +9,9 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "shape.h"
 
 namespace oomb {
-
-// A validated descriptor.
-struct Shape {
-  int hq, hkv, d, ps, ps_log2, c, n, keff, n_slots, rep_cap;
-  bool bf16;
-  float scale;  // resolved softmax scale
-};
 
 inline Geo make_geo(const Shape& s) {
   Geo g;
@@ -79,7 +73,5 @@ hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_s
 hipError_t launch_check_tables(const Shape& s, const int32_t* pt, const int32_t* sel, int32_t* counts,
                                int32_t* slot_uses, hipStream_t st);
 hipError_t launch_probe_mfma(int n_blocks, int iters, float* out, hipStream_t st);
-void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
-                           const int32_t* sel, float* host_dk, float* host_dv, int n_threads);
 
 }  // namespace oomb

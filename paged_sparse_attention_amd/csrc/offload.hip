@@ -21,8 +21,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <thread>
-#include <vector>
 
 #include "launch.h"
 #include "trace.h"
@@ -261,49 +259,6 @@ hipError_t launch_stage_tables(const Shape& s, int32_t* sel_stage, int32_t* pt_s
   hipLaunchKernelGGL(stage_tables_kernel, dim3((n_stage + 255) / 256), dim3(256), 0, st, sel_stage, nsel, pt_stage,
                      n_stage);
   return hipGetLastError();
-}
-
-// Host side of the gradient offload: compact block b of delta is added to its
-// (host slot, kv-head) block of the host pool.  Within one call every
-// destination block is distinct (a kv-head's selected pages are distinct and
-// none is a chunk page), so the threads never write the same element.
-void host_accumulate_grads(const Shape& s, const float* delta_dk, const float* delta_dv, const int32_t* pt,
-                           const int32_t* sel, float* host_dk, float* host_dv, int n_threads) {
-  const int nsel = s.hkv * s.keff, n_blocks = nsel + (s.c / s.ps) * s.hkv;
-  const int64_t blk = (int64_t)s.ps * s.d;
-  auto work = [&](int b0, int b1) {
-    for (int b = b0; b < b1; ++b) {
-      int h, logical;
-      if (b < nsel) {
-        h = b / s.keff;
-        logical = sel[b];
-        if (logical < 0 || logical >= s.n) continue;
-      } else {
-        h = (b - nsel) % s.hkv;
-        logical = s.n + (b - nsel) / s.hkv;
-      }
-      const int slot = pt[logical];
-      if (slot < 0 || slot >= s.n_slots) continue;
-      const int64_t off = ((int64_t)slot * s.hkv + h) * blk;
-      const float* dk = delta_dk + (int64_t)b * blk;
-      const float* dv = delta_dv + (int64_t)b * blk;
-      float* hk = host_dk + off;
-      float* hv = host_dv + off;
-      for (int64_t i = 0; i < blk; ++i) hk[i] += dk[i];
-      for (int64_t i = 0; i < blk; ++i) hv[i] += dv[i];
-    }
-  };
-  const int nt = std::max(1, std::min(n_threads, n_blocks));
-  if (nt == 1) {
-    work(0, n_blocks);
-    return;
-  }
-  std::vector<std::thread> pool;
-  pool.reserve(nt - 1);
-  for (int t = 1; t < nt; ++t)
-    pool.emplace_back(work, (int)((int64_t)n_blocks * t / nt), (int)((int64_t)n_blocks * (t + 1) / nt));
-  work(0, (int)((int64_t)n_blocks / nt));
-  for (std::thread& th : pool) th.join();
 }
 
 }  // namespace oomb
