@@ -80,7 +80,8 @@ typedef enum {
   OOMB_ERR_MISALIGNED = -5,  /* a device pointer is not 16-byte aligned */
   OOMB_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the *_workspace_bytes query */
   OOMB_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
-  OOMB_ERR_NOT_MAPPED = -8   /* host memory the device cannot address (oomb_host_view) */
+  OOMB_ERR_NOT_MAPPED = -8,  /* host memory the device cannot address (oomb_host_view) */
+  OOMB_ERR_SCRATCH_LIMIT = -9 /* the shape needs more scratch than oomb_select_topk_noalloc holds */
 } oomb_status;
 
 /* Host-side descriptor of one chunk step. */
@@ -124,6 +125,28 @@ size_t oomb_select_workspace_bytes(const oomb_desc* desc);
  * order, so repeated calls give identical bits. */
 int oomb_select_topk(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
                      float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* oomb_select_topk without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results and determinism as
+ * oomb_select_topk (the same kernels); the workspace is instead a scratch
+ * array that the library holds on each device it runs on, of
+ * OOMB_NOALLOC_SCRATCH_BYTES (4 MiB), resident until the process ends.  No
+ * device memory is allocated or freed by the call.
+ * Every call on one device uses that device's one scratch array: calls that
+ * can overlap on one device (unordered streams, several host threads) race
+ * and must be ordered by the caller.  The scratch holds the previous call's
+ * partial sums and scores; each call overwrites what it reads, so nothing
+ * needs clearing.
+ * Errors: the checks of oomb_select_topk, then OOMB_ERR_SCRATCH_LIMIT when
+ * oomb_select_workspace_bytes(desc) exceeds the scratch (Hkv * N up to about
+ * 917,000 at Hkv * D = 512, 785,000 at Hkv * D = 1024), all before any HIP
+ * call;
+ * OOMB_ERR_LAUNCH if the scratch's address cannot be obtained on the current
+ * device or a launch fails. */
+#define OOMB_NOALLOC_SCRATCH_BYTES (4u << 20)
+int oomb_select_topk_noalloc(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
+                             float* scores_out, void* stream);
 
 /* Fused forward (OOMB, section 2: attention over the selected pages plus the
  * local chunk).  For chunk token t and query head g, h = g / (Hq/Hkv), the key

@@ -57,6 +57,7 @@ def _load():
         "oomb_rep_update": (ctypes.c_int, [P, vp, vp, i32, i32, vp, vp]),
         "oomb_select_workspace_bytes": (sz, [P]),
         "oomb_select_topk": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "oomb_select_topk_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "oomb_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp]),
         "oomb_bwd_workspace_bytes": (sz, [P]),
         "oomb_attn_bwd": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
@@ -173,6 +174,15 @@ def oomb_select_topk(desc, q, rep, sel, scores_out, workspace, workspace_bytes=N
     _check(_L.oomb_select_topk(ctypes.byref(desc), _dev(q, io, "q"), _dev(rep, torch.float32, "rep"),
                                _dev(sel, torch.int32, "sel"), _dev(scores_out, torch.float32, "scores_out"),
                                _dev(workspace, None, "workspace"), nbytes, _stream(stream)))
+
+
+def oomb_select_topk_noalloc(desc, q, rep, sel, scores_out=None, stream=None):
+    """oomb_select_topk on the library's own per-device scratch: no workspace
+    argument, and nothing is allocated here either (see include/oomb.h)."""
+    io = _IO_DTYPE.get(desc.dtype)
+    _check(_L.oomb_select_topk_noalloc(ctypes.byref(desc), _dev(q, io, "q"), _dev(rep, torch.float32, "rep"),
+                                       _dev(sel, torch.int32, "sel"), _dev(scores_out, torch.float32, "scores_out"),
+                                       _stream(stream)))
 
 
 def oomb_attn_fwd(desc, q, k_pool, v_pool, page_table, sel, o, lse, stream=None):

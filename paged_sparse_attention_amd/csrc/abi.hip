@@ -76,6 +76,26 @@ OOMB_API int oomb_select_topk(const oomb_desc* desc, const void* q, const float*
   return launched(oomb::launch_select(s, q, rep, sel, scores_out, workspace, (hipStream_t)stream));
 }
 
+OOMB_API int oomb_select_topk_noalloc(const oomb_desc* desc, const void* q, const float* rep, int32_t* sel,
+                                      float* scores_out, void* stream) {
+  oomb::Shape s;
+  int rc = validate(desc, &s);
+  if (rc) return rc;
+  if ((rc = check_ptrs({q, rep}))) return rc;
+  if (s.keff > 0 && (rc = check_ptrs({sel}))) return rc;
+  if (scores_out && misaligned(scores_out)) return OOMB_ERR_MISALIGNED;
+  const oomb::SelectPlan p = oomb::select_plan(s);
+  if (p.bytes > oomb::kNoAllocScratchBytes) return OOMB_ERR_SCRATCH_LIMIT;
+  if (s.n == 0) return OOMB_OK;
+  (void)hipGetLastError();
+  void* ws = nullptr;
+  if (oomb::noalloc_scratch(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return OOMB_ERR_LAUNCH;
+  }
+  return launched(oomb::launch_select(s, q, rep, sel, scores_out, ws, (hipStream_t)stream));
+}
+
 OOMB_API int oomb_attn_fwd(const oomb_desc* desc, const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* page_table, const int32_t* sel, void* o, float* lse, void* stream) {
   oomb::Shape s;
@@ -260,6 +280,7 @@ OOMB_API const char* oomb_status_string(int status) {
     case OOMB_ERR_WORKSPACE: return "workspace missing or too small";
     case OOMB_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case OOMB_ERR_NOT_MAPPED: return "host memory that the device cannot address";
+    case OOMB_ERR_SCRATCH_LIMIT: return "the shape needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -50,6 +50,10 @@ hipError_t launch_rep_update(const Shape& s, const void* k_pool, const int32_t* 
                              float* rep, hipStream_t st);
 hipError_t launch_select(const Shape& s, const void* q, const float* rep, int32_t* sel, float* scores_out,
                          void* ws, hipStream_t st);
+// The allocation-free selection's per-device scratch (kNoAllocScratchBytes,
+// 256-byte aligned): its device address on the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)OOMB_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_fwd(const Shape& s, const void* q, const void* k_pool, const void* v_pool, const int32_t* pt,
                       const int32_t* sel, void* o, float* lse, hipStream_t st);
 hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const void* v_pool, const int32_t* pt,

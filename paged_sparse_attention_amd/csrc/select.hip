@@ -10,6 +10,8 @@
 //
 // All four kernels are HBM- or latency-bound; none uses atomics on global
 // memory, so every result is bitwise reproducible.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 #include "trace.h"
@@ -339,6 +341,33 @@ static hipError_t select_t(const Shape& s, const SelectPlan& p, const void* q, c
     hipLaunchKernelGGL(topk_kernel, dim3(s.hkv), dim3(1024), 0, st, (const float*)scores, s.n, s.keff, sel);
   }
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free selection (oomb_select_topk_noalloc): one
+// array per device, resident until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol, not a device address: the
+// address is taken once per device with hipGetSymbolAddress, with that device
+// current, and only that address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex lock;
+  static void* per_device[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = p;
+  }
+  *out = per_device[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_select(const Shape& s, const void* q, const float* rep, int32_t* sel, float* scores_out,

@@ -15,6 +15,7 @@ HEADER = os.path.join(ROOT, "include", "oomb.h")
 
 OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH = 0, -1, -2, -3, -4, -5, -6, -7
 NOT_MAPPED = -8
+SCRATCH_LIMIT = -9
 A = 0x10000        # a fake, 16-byte aligned device address
 B = 0x20000
 
@@ -39,7 +40,8 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert P.oomb_abi_version() == P.ABI_VERSION == 2
-    for code in (OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH, NOT_MAPPED):
+    for code in (OK, NULL_PTR, BAD_SHAPE, UNSUPPORTED, BAD_DTYPE, MISALIGNED, WORKSPACE, LAUNCH, NOT_MAPPED,
+                 SCRATCH_LIMIT):
         assert P.oomb_status_string(code) and P.oomb_status_string(code) != "unknown status"
     assert P.oomb_status_string(-99) == "unknown status"
 
@@ -119,6 +121,22 @@ def test_workspaces():
     assert L.oomb_attn_bwd(P.ctypes.byref(d), *args, None, wb, None) == WORKSPACE
     args[8] = None  # dq
     assert L.oomb_attn_bwd(P.ctypes.byref(d), *args, A, wb, None) == NULL_PTR
+
+
+def test_select_noalloc_checks():
+    """The allocation-free selection: the same argument checks as
+    oomb_select_topk, and shapes whose workspace exceeds the library's 4 MiB
+    scratch are rejected, all before any HIP call."""
+    L = P._L
+    d = good()
+    assert L.oomb_select_topk_noalloc(P.ctypes.byref(d), None, A, A, None, None) == NULL_PTR
+    assert L.oomb_select_topk_noalloc(P.ctypes.byref(d), A, A, None, None, None) == NULL_PTR
+    assert L.oomb_select_topk_noalloc(P.ctypes.byref(d), A, A, A, A + 4, None) == MISALIGNED
+    assert L.oomb_select_topk_noalloc(P.ctypes.byref(good(chunk_len=4000)), A, A, A, None, None) == BAD_SHAPE
+    big = good(n_prior_pages=300000, n_slots=300032)       # Hkv * N = 1.2 million scores
+    assert P.oomb_select_workspace_bytes(big) > 4 << 20
+    assert L.oomb_select_topk_noalloc(P.ctypes.byref(big), A, A, A, None, None) == SCRATCH_LIMIT
+    assert P.oomb_select_workspace_bytes(good(n_prior_pages=32768, n_slots=32800)) <= 4 << 20  # sparse-4m fits
 
 
 def test_rep_update_ranges():
