@@ -343,6 +343,12 @@ def layer_bench(args):
                                 eps=s.eps)
     del bits
     layer_bytes = torch.cuda.memory_allocated() - m0
+    nbytes = lambda *ts: sum(t.numel() * t.element_size() for t in ts)
+    # the parts of the layer that grow with the sequence: paged K/V and their
+    # gradients, representative vectors, selections, page table, rotary tables
+    seq_state = nbytes(layer.k_pool, layer.v_pool, layer.dk_pool, layer.dv_pool, layer.rep, layer.pt, layer.cos,
+                       layer.sin, *layer.sel)
+    held = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
     hip = HipEvents(P.hip_runtimes_loaded()[0], 2 * 16 * s.chunks)  # per pass: at most 16 launches a chunk
     fwd_ms, bwd_ms, attn_ms = [], [], []
@@ -388,8 +394,13 @@ def layer_bench(args):
                    "activations": "one chunk, forward re-run in the backward"},
         "gemm_tflops": gemm_flops / ((ms - attn) / 1e3) / 1e12,
         "attention_tflops": 14.0 * s.d * pairs / (attn / 1e3) / 1e12,
-        "device_bytes": {"layer": layer_bytes, "peak_allocated": torch.cuda.max_memory_allocated(),
-                         "inputs_x_dy": x.numel() * 2 + dy.numel() * 4},
+        # peak = what is held before the pass (inputs, layer) + the pass's
+        # fp32 [tokens][hidden] result (y in the forward, dx in the backward)
+        # + activations: one chunk's autograd graph and workspaces
+        "device_bytes": {"layer": layer_bytes, "layer_sequence_state": seq_state,
+                         "layer_fixed": layer_bytes - seq_state, "inputs_x_dy": x.numel() * 2 + dy.numel() * 4,
+                         "pass_result": tokens * s.hidden * 4, "peak_allocated": torch.cuda.max_memory_allocated(),
+                         "activation_peak": torch.cuda.max_memory_allocated() - held - tokens * s.hidden * 4},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)

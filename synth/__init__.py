@@ -301,4 +301,5 @@ LAYERS = {
     "layer-tiny": (11, Layer(hidden=256, hq=4, hkv=2, d=64, inter=512, ps=16, c=64, chunks=4, k=2)),
     "layer-tiny-d128": (13, Layer(hidden=256, hq=2, hkv=1, d=128, inter=384, ps=32, c=64, chunks=5, k=3)),
     "layer-qwen-64k": (12, Layer(hidden=3584, hq=28, hkv=4, d=128, inter=18944, ps=128, c=4096, chunks=16, k=64)),
+    "layer-qwen-256k": (14, Layer(hidden=3584, hq=28, hkv=4, d=128, inter=18944, ps=128, c=4096, chunks=64, k=64)),
 }
