@@ -189,9 +189,11 @@ class ChunkedDecoderLayer:
 
     # -- the two sweeps -----------------------------------------------------
     @torch.no_grad()
-    def forward(self, x):
+    def forward(self, x, queries=None):
         """x: bf16 [chunks*C][hidden].  Returns y fp32 [chunks*C][hidden]; keeps
-        the pools, the representative vectors and every chunk's selection."""
+        the pools, the representative vectors and every chunk's selection.
+        queries: a list that, when given, receives each chunk's post-rotary
+        bf16 queries (the ones the selection scored), for inspection."""
         w = self._weights()
         y = torch.empty((self.n_chunks * self.c, self.h), dtype=torch.float32, device=x.device)
         for i in range(self.n_chunks):
@@ -202,6 +204,8 @@ class ChunkedDecoderLayer:
             self.k_pool[s] = k.view(self.cp, self.ps, self.hkv, self.d).permute(0, 2, 1, 3)
             self.v_pool[s] = v.view(self.cp, self.ps, self.hkv, self.d).permute(0, 2, 1, 3)
             desc = self.descs[i]
+            if queries is not None:
+                queries.append(q.clone())
             oomb_select_topk(desc, q, self.rep, self.sel[i], None, self.ws_select)
             o, _ = self._attend(i, q)
             oomb_rep_update(desc, self.k_pool, self.pt, i * self.cp, self.cp, self.rep)
