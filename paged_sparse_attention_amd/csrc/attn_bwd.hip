@@ -14,8 +14,10 @@
 //      tiles of 32 rows, recomputing S = Q K^T and dP = dO V^T on MFMA, then
 //      dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T read transposed from the
 //      row-major LDS tiles).  When the rows are split over several workgroups
-//      for load balance, the first split adds into the pools in place and the
-//      others write partial sums to the workspace.
+//      for load balance (and split again in two for the chunk's key blocks,
+//      when an XCD would otherwise get too few of them to even out its last
+//      round), the first piece adds into the pools in place and the others
+//      write partial sums to the workspace.
 //   3. dq_kernel:   query-major, like the forward: S^T and dP^T per 32-key
 //      block of a K/V tile, dQ^T += K^T dS^T, written once per row.  With a
 //      row split, trailing workgroups of the same launch then add the other
@@ -51,7 +53,11 @@ struct BwdArgs {
                    // to it exactly and five zeros (the dK/dV kernel's bias operands, bf16 inputs)
   float* part_k;   // workspace [splits-1][Hkv][nkeys][D], scaled dK partials of splits 1..
   float* part_v;   // workspace [splits-1][Hkv][nkeys][D]
+  float* part2_k;  // workspace [splits][Hkv][nkeys - key0_sub][D], second halves of the chunk blocks' shares
+  float* part2_v;  //   (only when sub = 2)
   int splits;
+  int sub;         // 2: each share of a chunk key block is split again in two (KvPlan)
+  int key0_sub;    // first key of the chunk key blocks (a multiple of the workgroup's keys)
   Geo g;
   float scale_log2;
 };
@@ -137,13 +143,24 @@ template <typename T> constexpr int kv_waves() { return 4; }
 template <typename T> constexpr int kv_keys() { return kv_waves<T>() * 32; }  // keys per workgroup
 template <typename T, int D> constexpr int kv_bm() { return sizeof(T) == 2 && D == 64 ? 64 : 32; }  // rows per tile
 
+// Work of the dK/dV kernel: nkb key blocks per kv-head, the first nprior of
+// which hold prior keys (every query row sees them), the rest chunk keys (only
+// the rows at or after them).  Each key block's rows are split into `splits`
+// shares.  When the groups (kv-head, share) divide evenly over the 8 XCDs
+// (`ordered`, gpx groups per XCD), and an XCD would get fewer chunk key blocks
+// than two per workgroup slot (32 CUs x 2), each share of a chunk key block is
+// split again in two (sub = 2): the chunk blocks, which end the kernel, then
+// come in pieces of at most half a prior block's work, and the last round
+// evens out.
 struct KvPlan {
-  int nkb, splits;
+  int nkb, splits, nprior, sub, gpx, items;
+  bool ordered;
 };
 
 __host__ __device__ inline KvPlan kv_plan(const Geo& g, int keys_per_wg) {
   KvPlan p;
-  const int nkeys = (g.keff << g.ps_log2) + g.c;
+  const int pk = g.keff << g.ps_log2;
+  const int nkeys = pk + g.c;
   p.nkb = (nkeys + keys_per_wg - 1) / keys_per_wg;
   const int items = p.nkb * g.hkv;
   // at least three rounds of two workgroups per CU, and never fewer than four
@@ -152,6 +169,12 @@ __host__ __device__ inline KvPlan kv_plan(const Geo& g, int keys_per_wg) {
   // the extra partial sums costing less than the balance they buy
   int s = (1536 + items - 1) / items;
   p.splits = s < 4 ? 4 : (s > 8 ? 8 : s);
+  p.nprior = min(p.nkb, (pk + keys_per_wg - 1) / keys_per_wg);
+  const int total = p.nkb * p.splits * g.hkv, per = total / 8;
+  p.ordered = total % 8 == 0 && per % p.nkb == 0 && p.nprior > 0 && p.nprior < p.nkb;
+  p.gpx = p.ordered ? per / p.nkb : 0;
+  p.sub = p.ordered && p.gpx * (p.nkb - p.nprior) < 128 ? 2 : 1;
+  p.items = g.hkv * p.splits * (p.nprior + (p.nkb - p.nprior) * p.sub);
   return p;
 }
 
@@ -202,39 +225,38 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 
   const Geo& g = a.g;
   const KvPlan plan = kv_plan(g, KEYS);
-  // Work items are (row-share group = kv-head and split, key block).  Each
-  // XCD takes whole groups, so the workgroups that run together on it stream
-  // the same shares of query rows through its L2.  Within an XCD the key
-  // blocks that hold prior keys (every row sees them: the heaviest, all alike)
-  // go first, group by group, then the chunk's key blocks, which fewer rows
-  // see, heaviest first with the groups alternating: the light ones end the
-  // kernel.  Shapes whose items do not split evenly into whole groups per XCD
-  // take contiguous ranges of items per XCD instead.
-  int h, sp, kblk;
-  {
-    const int total = plan.nkb * plan.splits * g.hkv, per = total / 8;
-    const int nprior = min(plan.nkb, ((g.keff << g.ps_log2) + KEYS - 1) / KEYS);
-    if (total % 8 == 0 && per % plan.nkb == 0 && nprior > 0 && nprior < plan.nkb) {
-      const int x = blockIdx.x % 8, j = blockIdx.x / 8, gpx = per / plan.nkb;
-      int grp;
-      if (j < gpx * nprior) {
-        grp = j / nprior;
-        kblk = j % nprior;
-      } else {
-        const int jl = j - gpx * nprior;
-        grp = jl % gpx;
-        kblk = nprior + jl / gpx;
-      }
-      const int gi = x * gpx + grp;
-      h = gi / plan.splits;
-      sp = gi % plan.splits;
+  // Work items are (row-share group = kv-head and split, key block), and for
+  // chunk key blocks with sub = 2 also the half of the share.  Each XCD takes
+  // whole groups, so the workgroups that run together on it stream the same
+  // shares of query rows through its L2.  Within an XCD the key blocks that
+  // hold prior keys (every row sees them: the heaviest, all alike) go first,
+  // group by group, then the chunk's key blocks, which fewer rows see,
+  // heaviest first with the groups (and halves) alternating: the light ones
+  // end the kernel.  Shapes whose items do not split evenly into whole groups
+  // per XCD take contiguous ranges of items per XCD instead.
+  int h, sp, kblk, half = 0;
+  if (plan.ordered) {
+    const int x = blockIdx.x % 8, j = blockIdx.x / 8, gpx = plan.gpx, nprior = plan.nprior;
+    int grp;
+    if (j < gpx * nprior) {
+      grp = j / nprior;
+      kblk = j % nprior;
     } else {
-      const int item = xcd_remap(blockIdx.x, total);
-      h = item / (plan.nkb * plan.splits);
-      kblk = item % plan.nkb;
-      sp = (item / plan.nkb) % plan.splits;
+      const int jl = j - gpx * nprior, w = gpx * plan.sub;
+      grp = jl % gpx;
+      half = (jl % w) / gpx;
+      kblk = nprior + jl / w;
     }
+    const int gi = x * gpx + grp;
+    h = gi / plan.splits;
+    sp = gi % plan.splits;
+  } else {
+    const int item = xcd_remap(blockIdx.x, plan.items);
+    h = item / (plan.nkb * plan.splits);
+    kblk = item % plan.nkb;
+    sp = (item / plan.nkb) % plan.splits;
   }
+  const int nhalf = kblk >= plan.nprior ? plan.sub : 1;  // pieces of this block's share
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hh = lane >> 5;
@@ -274,8 +296,9 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   const int t_first = jb < pk ? 0 : ((jb - pk) / BM) * BM;
   const int tiles_per_head = (g.c - t_first + BM - 1) / BM;
   const int ntile_all = tiles_per_head * g.G;
-  const int tile_lo = (int)((int64_t)ntile_all * sp / plan.splits);
-  const int tile_hi = (int)((int64_t)ntile_all * (sp + 1) / plan.splits);
+  const int nsh = plan.splits * nhalf, ish = sp * nhalf + half;  // this piece among the block's pieces
+  const int tile_lo = (int)((int64_t)ntile_all * ish / nsh);
+  const int tile_hi = (int)((int64_t)ntile_all * (ish + 1) / nsh);
   const int ntiles = tile_hi - tile_lo;
   auto tile_head = [&](int j) { return (tile_lo + j) / tiles_per_head; };
   auto tile_t0 = [&](int j) { return t_first + ((tile_lo + j) % tiles_per_head) * BM; };
@@ -426,7 +449,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
 
   if (!key_ok) return;
   const float sc = g.scale;
-  if (sp == 0) {  // the first split adds straight into the pools; the split reduction adds the rest after it
+  if (sp == 0 && half == 0) {  // the first split adds straight into the pools; the split reduction adds the rest after it
     float* dkp = a.dk + koff;
     float* dvp = a.dv + koff;
 #pragma unroll
@@ -445,7 +468,14 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
         *reinterpret_cast<f32x4*>(dvp + d) = ov;
       }
   } else {
-    const int64_t base = (((int64_t)(sp - 1) * g.hkv + h) * nkeys + my_key) * D;
+    // first halves (and whole shares) of splits 1..: part_k/v [splits-1][Hkv][nkeys][D];
+    // second halves: part2_k/v [splits][Hkv][nkeys - key0_sub][D]
+    const int slot = half == 0 ? sp - 1 : sp;
+    const int key0 = half == 0 ? 0 : a.key0_sub;
+    const int nk = nkeys - key0;
+    const int64_t base = (((int64_t)slot * g.hkv + h) * nk + (my_key - key0)) * D;
+    float* pk_out = half == 0 ? a.part_k : a.part2_k;
+    float* pv_out = half == 0 ? a.part_v : a.part2_v;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -457,15 +487,16 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
           wk[i] = sc * dkacc[db][4 * e4 + i];
           wv[i] = dvacc[db][4 * e4 + i];
         }
-        *reinterpret_cast<f32x4*>(a.part_k + base + d) = wk;
-        *reinterpret_cast<f32x4*>(a.part_v + base + d) = wv;
+        *reinterpret_cast<f32x4*>(pk_out + base + d) = wk;
+        *reinterpret_cast<f32x4*>(pv_out + base + d) = wv;
       }
   }
 }
 
 // dk_pool / dv_pool += sum of the partials of splits 1 .. splits-1, in split
-// order (split 0 has already added its share in place); float4 group i of the
-// [Hkv][keys][D] key list.  Runs after dkdv_kernel has finished (a later
+// order, then for the chunk key blocks split in halves those of the second
+// halves of shares 0 .. splits-1 (the first half of share 0 has already added
+// in place); float4 group i of the [Hkv][keys][D] key list.  Runs after dkdv_kernel has finished (a later
 // launch on the same stream).
 template <int D>
 __device__ __forceinline__ void kv_reduce_group(const BwdArgs& a, int64_t i) {
@@ -481,6 +512,15 @@ __device__ __forceinline__ void kv_reduce_group(const BwdArgs& a, int64_t i) {
   for (int s = 1; s < a.splits - 1; ++s) {
     sk += *reinterpret_cast<const f32x4*>(a.part_k + s * stride + src);
     sv += *reinterpret_cast<const f32x4*>(a.part_v + s * stride + src);
+  }
+  if (a.sub == 2 && jj >= a.key0_sub) {
+    const int nk2 = nkeys - a.key0_sub;
+    const int64_t stride2 = (int64_t)g.hkv * nk2 * D;
+    const int64_t src2 = ((int64_t)h * nk2 + (jj - a.key0_sub)) * D + d;
+    for (int s = 0; s < a.splits; ++s) {
+      sk += *reinterpret_cast<const f32x4*>(a.part2_k + s * stride2 + src2);
+      sv += *reinterpret_cast<const f32x4*>(a.part2_v + s * stride2 + src2);
+    }
   }
   const int64_t dst = key_offset<D>(g, a.pt, a.sel, h, jj) + d;
   f32x4 ok = *reinterpret_cast<f32x4*>(a.dk + dst);
@@ -664,11 +704,18 @@ BwdPlan bwd_plan(const Shape& s) {
   p.off_bias = 2 * rowvec;
   size_t off = 2 * rowvec + ((((size_t)s.hq * s.c * 32) + 255) & ~(size_t)255);
   p.splits = kp.splits;
+  p.sub = kp.sub;
+  p.key0_sub = kp.nprior * (s.bf16 ? kv_keys<__bf16>() : kv_keys<float>());
   p.off_part_k = off;
   const size_t part = kp.splits > 1 ? (size_t)(kp.splits - 1) * s.hkv * nkeys * s.d * 4 : 0;
   off += (part + 255) & ~(size_t)255;
   p.off_part_v = off;
   off += (part + 255) & ~(size_t)255;
+  const size_t part2 = kp.sub == 2 ? (size_t)kp.splits * s.hkv * (nkeys - (size_t)p.key0_sub) * s.d * 4 : 0;
+  p.off_part2_k = off;
+  off += (part2 + 255) & ~(size_t)255;
+  p.off_part2_v = off;
+  off += (part2 + 255) & ~(size_t)255;
   p.bytes = off;
   return p;
 }
@@ -685,7 +732,7 @@ static hipError_t bwd_t(const BwdArgs& a, hipStream_t st) {
   const KvPlan kp = kv_plan(a.g, kv_keys<T>());
   {
     Traced tr(st, "dkdv_kernel");
-    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(kp.nkb * kp.splits * a.g.hkv), dim3(kv_waves<T>() * 64), 0, st, a);
+    hipLaunchKernelGGL((dkdv_kernel<T, D>), dim3(kp.items), dim3(kv_waves<T>() * 64), 0, st, a);
   }
   const int qrows = a.g.c * a.g.G;
   {
@@ -719,7 +766,11 @@ hipError_t launch_bwd(const Shape& s, const void* q, const void* k_pool, const v
   a.bias = (__bf16*)((char*)ws + p.off_bias);
   a.part_k = (float*)((char*)ws + p.off_part_k);
   a.part_v = (float*)((char*)ws + p.off_part_v);
+  a.part2_k = (float*)((char*)ws + p.off_part2_k);
+  a.part2_v = (float*)((char*)ws + p.off_part2_v);
   a.splits = p.splits;
+  a.sub = p.sub;
+  a.key0_sub = p.key0_sub;
   a.g = make_geo(s);
   a.scale_log2 = s.scale * kLog2e;
   if (s.bf16) return s.d == 128 ? bwd_t<__bf16, 128>(a, st) : bwd_t<__bf16, 64>(a, st);

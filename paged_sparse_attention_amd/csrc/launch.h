@@ -41,7 +41,11 @@ struct BwdPlan {
   size_t off_lse2;                // lse * log2(e) per (head, token), fp32 [Hq][C]
   size_t off_bias;                // dK/dV bias operands per (head, token), bf16 [Hq][C][16]
   size_t off_part_k, off_part_v;  // dK / dV partial sums of row splits 1.., fp32 [splits-1][Hkv][nkeys][D]
+  size_t off_part2_k, off_part2_v;  // second halves of the chunk key blocks' shares (sub = 2),
+                                    // fp32 [splits][Hkv][nkeys - key0_sub][D]
   int splits;                     // workgroups sharing one key block's query rows
+  int sub;                        // 2: each share of a chunk key block is split again in two
+  int key0_sub;                   // first key of the chunk key blocks
   size_t bytes;
 };
 BwdPlan bwd_plan(const Shape& s);

@@ -236,23 +236,34 @@ def test_layer_op_argument_checks():
     assert L.oomb_swiglu_bwd(A, A, A, B, B + 2, 8, None) == MISALIGNED
 
 
-@pytest.mark.parametrize("kw,splits", [
-    (dict(), 4),                                            # 96 key blocks x 4 kv-heads: 4 splits
-    (dict(chunk_len=8192, n_prior_pages=32768, top_k=128, n_slots=32832), 4),  # 192 blocks: at least 4
-    (dict(chunk_len=256, n_prior_pages=12, top_k=4, n_slots=14), 8),          # 12 blocks: capped at 8
-    (dict(chunk_len=2048, n_prior_pages=48, top_k=48, n_slots=64), 6),           # 64 blocks: 1536 / 256
+@pytest.mark.parametrize("kw,splits,sub", [
+    (dict(), 4, 2),                                            # 96 key blocks x 4 kv-heads: 4 splits
+    (dict(chunk_len=8192, n_prior_pages=32768, top_k=128, n_slots=32832), 4, 1),  # 192 blocks: at least 4
+    (dict(chunk_len=256, n_prior_pages=12, top_k=4, n_slots=14), 8, 2),          # 12 blocks: capped at 8
+    (dict(chunk_len=2048, n_prior_pages=48, top_k=48, n_slots=64), 6, 2),           # 64 blocks: 1536 / 256
+    (dict(n_q_heads=21, n_kv_heads=3), 6, 1),                # 288 blocks x heads: no whole groups per XCD
 ])
-def test_bwd_workspace_holds_the_split_partials(kw, splits):
+def test_bwd_workspace_holds_the_split_partials(kw, splits, sub):
     # Dt, lse*log2(e) and the rows' bias operands (32 bytes a row), then the
     # partial dK and dV sums of every row split but the first, each
     # [Hkv][K_eff*ps + C][D] fp32, every part rounded up to 256 bytes.
     # Rows of a key block are split over max(4, ceil(1536 / (key blocks x
     # kv-heads))) workgroups, at most 8; a key block is 128 keys (bf16).
+    # When the (kv-head, split) groups divide evenly over 8 XCDs and an XCD
+    # gets fewer than 128 chunk key blocks, each share of a chunk key block is
+    # halved, and the second halves' sums take [splits][Hkv][chunk block keys][D]
+    # more for dK and for dV.
     d = good(**kw)
     hq, hkv, dd, c = d.n_q_heads, d.n_kv_heads, d.head_dim, d.chunk_len
-    keys = min(d.top_k, d.n_prior_pages) * d.page_size + c
+    pk = min(d.top_k, d.n_prior_pages) * d.page_size
+    keys = pk + c
     blocks = -(-keys // 128)
     assert min(8, max(4, -(-1536 // (blocks * hkv)))) == splits
+    nprior = min(blocks, -(-pk // 128))
+    total = blocks * splits * hkv
+    ordered = total % 8 == 0 and (total // 8) % blocks == 0 and 0 < nprior < blocks
+    assert (2 if ordered and (total // 8 // blocks) * (blocks - nprior) < 128 else 1) == sub
     up = lambda n: (n + 255) // 256 * 256
     part = up((splits - 1) * hkv * keys * dd * 4)
-    assert P.oomb_bwd_workspace_bytes(d) == 2 * up(hq * c * 4) + up(hq * c * 32) + 2 * part
+    part2 = up(splits * hkv * (keys - nprior * 128) * dd * 4) if sub == 2 else 0
+    assert P.oomb_bwd_workspace_bytes(d) == 2 * up(hq * c * 4) + up(hq * c * 32) + 2 * part + 2 * part2
