@@ -354,6 +354,13 @@ int oomb_abi_version(void);
  * Process-wide state: not for concurrent use from several host threads. */
 int oomb_trace_events(void* const* events, int capacity);
 
+/* Restrict kernel tracing to the launches of one kernel, named as
+ * oomb_trace_kernel reports them (for example "dkdv_kernel"); other launches
+ * record no events and take no slots.  NULL lifts the restriction.  The name
+ * is copied.  Returns OOMB_ERR_BAD_SHAPE for an empty name or one of 64 bytes
+ * or more.  Process-wide, like oomb_trace_events. */
+int oomb_trace_only(const char* kernel);
+
 /* Launches recorded since the last oomb_trace_events call, or minus the
  * hipError_t of the first event record that failed. */
 int oomb_trace_count(void);

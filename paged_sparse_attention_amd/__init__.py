@@ -81,6 +81,7 @@ def _load():
         "oomb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "oomb_abi_version": (ctypes.c_int, []),
         "oomb_trace_events": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
+        "oomb_trace_only": (ctypes.c_int, [ctypes.c_char_p]),
         "oomb_trace_count": (ctypes.c_int, []),
         "oomb_trace_kernel": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -324,6 +325,11 @@ def oomb_trace_events(events, capacity=None):
         _check(_L.oomb_trace_events(None, 0))
         return
     _check(_L.oomb_trace_events(ctypes.cast(events, ctypes.c_void_p), len(events) if capacity is None else capacity))
+
+
+def oomb_trace_only(kernel):
+    """Record only the launches of the named kernel (None: every launch)."""
+    _check(_L.oomb_trace_only(None if kernel is None else kernel.encode()))
 
 
 def oomb_trace_count() -> int:

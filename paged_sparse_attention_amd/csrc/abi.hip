@@ -297,6 +297,18 @@ OOMB_API int oomb_trace_events(void* const* events, int capacity) {
   return OOMB_OK;
 }
 
+OOMB_API int oomb_trace_only(const char* kernel) {
+  oomb::TraceState& t = oomb::trace_state();
+  if (!kernel) {
+    t.only[0] = 0;
+    return OOMB_OK;
+  }
+  const size_t n = strlen(kernel);
+  if (n == 0 || n >= sizeof(t.only)) return OOMB_ERR_BAD_SHAPE;
+  memcpy(t.only, kernel, n + 1);
+  return OOMB_OK;
+}
+
 OOMB_API int oomb_trace_count(void) {
   const oomb::TraceState& t = oomb::trace_state();
   return t.error ? -t.error : t.count;

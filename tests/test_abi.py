@@ -267,3 +267,15 @@ def test_bwd_workspace_holds_the_split_partials(kw, splits, sub):
     part = up((splits - 1) * hkv * keys * dd * 4)
     part2 = up(splits * hkv * (keys - nprior * 128) * dd * 4) if sub == 2 else 0
     assert P.oomb_bwd_workspace_bytes(d) == 2 * up(hq * c * 4) + up(hq * c * 32) + 2 * part + 2 * part2
+
+
+def test_trace_filter_arguments():
+    # host-only state: the name is checked and copied, nothing is launched
+    L = P._L
+    assert L.oomb_trace_only(b"dkdv_kernel") == OK
+    assert L.oomb_trace_only(b"") == BAD_SHAPE
+    assert L.oomb_trace_only(b"k" * 63) == OK
+    assert L.oomb_trace_only(b"k" * 64) == BAD_SHAPE
+    assert L.oomb_trace_only(None) == OK
+    P.oomb_trace_only("fwd_kernel")
+    P.oomb_trace_only(None)
