@@ -147,8 +147,8 @@ template <typename T, int D> constexpr int kv_bm() { return sizeof(T) == 2 && D 
 // which hold prior keys (every query row sees them), the rest chunk keys (only
 // the rows at or after them).  Each key block's rows are split into `splits`
 // shares.  When the groups (kv-head, share) divide evenly over the 8 XCDs
-// (`ordered`, gpx groups per XCD), and an XCD would get fewer chunk key blocks
-// than two per workgroup slot (32 CUs x 2), each share of a chunk key block is
+// (`ordered`, gpx groups per XCD), and an XCD would get at most two chunk key
+// blocks per workgroup slot (32 CUs x 2), each share of a chunk key block is
 // split again in two (sub = 2): the chunk blocks, which end the kernel, then
 // come in pieces of at most half a prior block's work, and the last round
 // evens out.
@@ -173,7 +173,7 @@ __host__ __device__ inline KvPlan kv_plan(const Geo& g, int keys_per_wg) {
   const int total = p.nkb * p.splits * g.hkv, per = total / 8;
   p.ordered = total % 8 == 0 && per % p.nkb == 0 && p.nprior > 0 && p.nprior < p.nkb;
   p.gpx = p.ordered ? per / p.nkb : 0;
-  p.sub = p.ordered && p.gpx * (p.nkb - p.nprior) < 128 ? 2 : 1;
+  p.sub = p.ordered && p.gpx * (p.nkb - p.nprior) <= 128 ? 2 : 1;
   p.items = g.hkv * p.splits * (p.nprior + (p.nkb - p.nprior) * p.sub);
   return p;
 }
