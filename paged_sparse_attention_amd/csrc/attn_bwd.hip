@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
   // keys past the list are clamped to its last key (finite data, zero weight below)
   ks.load((const T*)a.k, wave, lane, tid,
           [&](int r) -> int64_t { return key_offset<D>(g, a.pt, a.sel, h, min(jb + r, nkeys - 1)); });
-  if constexpr (kKeysInLds) wait_vmem_le(0);
+  vmem_drain();  // the K tile (LDS) and the V^T fragments (registers) have landed
 
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -328,13 +328,14 @@ __global__ __launch_bounds__(kv_waves<T>() * 64, 2) void dkdv_kernel(BwdArgs a) 
       }
     }
     if constexpr (kBias) {
-      // 32 bytes a row: lane l of a load carries half l % 2 of row l / 2
+      // 32 bytes a row: lane l of a load carries half l % 2 of row l / 2 (a
+      // wave-uniform base and a lane offset, which need no 64-bit lane address)
       if (wave == 0) {
+        const __bf16* brow = a.bias + ((int64_t)(h * g.G + gi) * g.c + t0) * 16;
 #pragma unroll
         for (int r0 = 0; r0 < 2 * BM; r0 += 64) {
-          const int64_t i = (int64_t)(h * g.G + gi) * g.c + t0 + min((r0 + lane) / 2, tmax);
-          __builtin_amdgcn_global_load_lds((gbl_void*)(a.bias + i * 16 + ((r0 + lane) & 1) * 8),
-                                           (lds_void*)&rbias[j % QD::NS][r0 / 2][0], 16, 0, 0);
+          const unsigned boff = (unsigned)(min((r0 + lane) / 2, tmax) * 32 + ((r0 + lane) & 1) * 16);
+          lds_load16(brow, boff, &rbias[j % QD::NS][r0 / 2][0]);
         }
       }
     }
@@ -600,6 +601,7 @@ __global__ __launch_bounds__(dq_waves<T>() * 64) void dq_kernel(BwdArgs a) {
   f32x16 qacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) qacc[db] = zero16();
+  vmem_drain();  // the Q and dO fragments and the row statistics are in registers before the key loop
 
   // The key loop, once per kind of page lookup (see Bool).
   auto run = [&](auto cached_tag) {

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kFwdWaves * 64) void fwd_pipe_kernel(FwdArgs a) {
   typedef __bf16 T;
   typedef Mma<T> M;
   constexpr int BN = 64, NT = kFwdWaves * 64;
-  typedef Ring<T, D, BN, NT, kPipeSlots> KV;
+  typedef Ring<T, D, BN, NT, kPipeSlots, false> KV;  // builtin loads (see Ring)
   typedef typename KV::TL TL;
   constexpr int KS = M::KS, KL = M::KL;
   constexpr int PD = kPipeSlots - 1;  // tiles issued ahead of the one whose V is read

@@ -36,6 +36,52 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
+// Direct global -> LDS loads issued through inline asm (lane l of a wave
+// writes bytes [n l, n l + n) of the block at the wave-uniform LDS address
+// `lds`; no registers are written).  The compiler cannot tell which LDS bytes
+// such a load writes, so after one it makes the next LDS read of any tile wait
+// for every load still in flight: with the builtin, a ring's tiles in flight
+// ahead of their use are waited for at the first read of the tile in use.
+// Issued as asm the loads are invisible to it, and a kernel waits for its own
+// (wait_vmem_le, counting this wave's loads issued later) before the barrier
+// that publishes a tile.  M0 holds the LDS address (one wait state before the
+// load reads it) and is restored afterwards.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)__builtin_amdgcn_readfirstlane(
+      (int)(unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  return (const void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
+}
+// 16 bytes a lane from the lane's own global address
+__device__ __forceinline__ void lds_load16(const void* gptr, const void* lds) {
+  int save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(gptr), "s"(lds_addr(lds))
+      : "memory");
+}
+// 16 bytes a lane from a wave-uniform base plus the lane's byte offset
+__device__ __forceinline__ void lds_load16(const void* base, unsigned byte_off, const void* lds) {
+  int save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(byte_off), "s"(uniform_ptr(base)), "s"(lds_addr(lds))
+      : "memory");
+}
+// 4 bytes a lane
+__device__ __forceinline__ void lds_load4(const void* gptr, const void* lds) {
+  int save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save)
+               : "v"(gptr), "s"(lds_addr(lds))
+               : "memory");
+}
+
 template <typename T, int D, int BR> struct Tile;
 
 template <int D, int BR> struct Tile<__bf16, D, BR> {
@@ -64,7 +110,7 @@ template <int D, int BR> struct Tile<__bf16, D, BR> {
       const int q = b * 64 + lane;
       const int r = q / SLOTS, p = q % SLOTS;
       const int c = p < CPR ? (p ^ flip(r)) : 0;
-      __builtin_amdgcn_global_load_lds((gbl_void*)(src + off(r) + c * VEC), (lds_void*)(rm + b * 512), 16, 0, 0);
+      lds_load16(src + off(r) + c * VEC, rm + b * 512);
     }
   }
   // (2s + hh) ^ flip(row) == 2s + (hh ^ flip(row)): s only adds an immediate offset
@@ -145,6 +191,12 @@ template <int D, int BR, int NT> struct Stager {
   }
 };
 
+// Waits for every vector-memory operation of this wave, as an instruction the
+// compiler sees (unlike wait_vmem_le): afterwards it knows that the registers
+// loaded before are ready, and does not wait for them again inside a key loop,
+// where that wait would also wait for the ring's loads in flight.
+__device__ __forceinline__ void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
 // Waits until at most n of this wave's vector-memory operations are still in
 // flight (direct-to-LDS loads included); n is clamped to the counter's range.
 __device__ __forceinline__ void wait_vmem_le(int n) {
@@ -178,7 +230,11 @@ template <typename TL> struct BlockCount<TL, true> {
 //     load(j + PD) if it exists               -- refills the slot of tile j - 1
 //     read tiles ta(j), tb(j)
 
-template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2> struct Ring {
+// ASM: direct loads through inline asm (above).  The forward keeps the
+// builtin: its key loop, at the register limit, is compiled with spill
+// reloads between the asm loads, each of which waits for the loads issued
+// before it.
+template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2, bool ASM = true> struct Ring {
   typedef Tile<T, D, BR> TL;
   static constexpr bool kDirect = sizeof(T) == 2;
   static constexpr int NS = NSLOTS;           // slots
@@ -208,8 +264,13 @@ template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2
         const int r = q / TL::SLOTS, p = q % TL::SLOTS;
         const int c = p < TL::CPR ? (p ^ TL::flip(r)) : 0;
         const int64_t o = off(r) + c * TL::VEC;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(srca + o), (lds_void*)(da + blk * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(srcb + o), (lds_void*)(db + blk * 512), 16, 0, 0);
+        if constexpr (ASM) {
+          lds_load16(srca + o, da + blk * 512);
+          lds_load16(srcb + o, db + blk * 512);
+        } else {
+          __builtin_amdgcn_global_load_lds((gbl_void*)(srca + o), (lds_void*)(da + blk * 512), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gbl_void*)(srcb + o), (lds_void*)(db + blk * 512), 16, 0, 0);
+        }
       }
     } else {
       sa.load((const float*)srca, tid, off);
@@ -253,8 +314,13 @@ template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2
     for (int i = 0; i < NBW; ++i) {
       const int blk = wave + i * NW;
       if (blk < TL::BLOCKS) {
-        __builtin_amdgcn_global_load_lds((gbl_void*)(a0 + l.off[i]), (lds_void*)(da + blk * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(b0 + l.off[i]), (lds_void*)(db + blk * 512), 16, 0, 0);
+        if constexpr (ASM) {
+          lds_load16(a0, (unsigned)l.off[i] * (unsigned)sizeof(T), da + blk * 512);
+          lds_load16(b0, (unsigned)l.off[i] * (unsigned)sizeof(T), db + blk * 512);
+        } else {
+          __builtin_amdgcn_global_load_lds((gbl_void*)(a0 + l.off[i]), (lds_void*)(da + blk * 512), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gbl_void*)(b0 + l.off[i]), (lds_void*)(db + blk * 512), 16, 0, 0);
+        }
       }
     }
   }
@@ -273,7 +339,7 @@ template <typename T, int D, int BR, int NT, int NSLOTS = sizeof(T) == 2 ? 3 : 2
 // One 32-bit value per lane straight from global memory to LDS (lane l writes
 // dst[l]); lanes outside exec write nothing.
 __device__ __forceinline__ void load_lds_dword(const float* src, float* dst_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)src, (lds_void*)dst_wave_base, 4, 0, 0);
+  lds_load4(src, dst_wave_base);
 }
 
 }  // namespace oomb
