@@ -10,7 +10,7 @@ import numpy as np
 
 from synth import Problem
 
-N_CASES = 40
+N_CASES = 64
 SEED = 20261203
 
 
