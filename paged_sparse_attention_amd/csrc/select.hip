@@ -167,29 +167,56 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ r
 // many keys equal to T are taken; a final pass in page order emits every page
 // with key > T and the lowest-index pages with key == T, so the output is
 // ascending and ties go to the lower page.  One 1024-thread workgroup per head.
+// With R > 0 each thread loads its keys (pages tid + 1024 r, r < R) once, all
+// loads in flight together, and every pass reads them from registers; R = 0
+// re-reads the scores from memory in each pass (N > 1024 * 32).  Each wave
+// counts into its own LDS histogram: the leading digits of the scores are
+// shared by most pages, and one histogram would make all 16 waves' atomic adds
+// wait on the same few bins.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t b = __float_as_uint(f == 0.f ? 0.f : f);  // -0 and +0 are one key
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ scores, int n, int k,
-                                                    int32_t* __restrict__ sel) {
-  __shared__ uint32_t hist[256];
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores, int n, int k,
+                                                            int32_t* __restrict__ sel) {
+  __shared__ uint32_t hist[kTopkWaves][256];
   __shared__ uint32_t sh_digit, sh_krem;
-  __shared__ uint32_t wave_tot[2][16];
+  __shared__ uint32_t wave_tot[2][kTopkWaves];
   const int h = blockIdx.x;
   const float* s = scores + (int64_t)h * n;
   int32_t* out = sel + (int64_t)h * k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  uint32_t kr[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = tid + kTopkThreads * r;
+      kr[r] = i < n ? order_key(s[i]) : 0u;
+    }
+  }
+
   uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+    for (int b = tid; b < kTopkWaves * 256; b += kTopkThreads) (&hist[0][0])[b] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) {
-      const uint32_t key = order_key(s[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int i = tid + kTopkThreads * r;
+        if (i < n && (kr[r] & mask) == prefix) atomicAdd(&hist[wave][(kr[r] >> shift) & 255u], 1u);
+      }
+    } else {
+      for (int i = tid; i < n; i += kTopkThreads) {
+        const uint32_t key = order_key(s[i]);
+        if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (wave == 0) {
@@ -197,7 +224,9 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
       uint32_t c[4], local = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c[i] = hist[255 - 4 * lane - i];
+        c[i] = 0;
+#pragma unroll
+        for (int w = 0; w < kTopkWaves; ++w) c[i] += hist[w][255 - 4 * lane - i];
         local += c[i];
       }
       uint32_t incl = local;
@@ -227,12 +256,10 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     __syncthreads();
   }
   const uint32_t T = prefix;
-  // emit in page order
+  // emit in page order, 1024 pages at a time
   uint32_t out_base = 0, eq_base = 0;
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int c0 = 0; c0 < n; c0 += 1024) {
-    const int i = c0 + tid;
-    const uint32_t key = i < n ? order_key(s[i]) : 0u;
+  auto emit = [&](int i, uint32_t key) {
     const bool gt = i < n && key > T;
     const bool eq = i < n && key == T;
     const uint64_t beq = __ballot(eq);
@@ -240,7 +267,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     __syncthreads();
     uint32_t eq_rank = eq_base + __popcll(beq & below);
     uint32_t eq_all = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < kTopkWaves; ++w) {
       if (w < wave) eq_rank += wave_tot[0][w];
       eq_all += wave_tot[0][w];
     }
@@ -250,7 +277,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     __syncthreads();
     uint32_t pos = out_base + __popcll(btk & below);
     uint32_t tk_all = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < kTopkWaves; ++w) {
       if (w < wave) pos += wave_tot[1][w];
       tk_all += wave_tot[1][w];
     }
@@ -258,6 +285,18 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     out_base += tk_all;
     eq_base += eq_all;
     __syncthreads();
+  };
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r * kTopkThreads >= n) break;  // uniform
+      emit(r * kTopkThreads + tid, kr[r]);
+    }
+  } else {
+    for (int c0 = 0; c0 < n; c0 += kTopkThreads) {
+      const int i = c0 + tid;
+      emit(i, i < n ? order_key(s[i]) : 0u);
+    }
   }
 }
 
@@ -338,7 +377,12 @@ static hipError_t select_t(const Shape& s, const SelectPlan& p, const void* q, c
     hipLaunchKernelGGL(identity_sel_kernel, dim3(grid), dim3(256), 0, st, s.n, s.hkv, sel);
   } else {
     Traced tr(st, "topk_kernel");
-    hipLaunchKernelGGL(topk_kernel, dim3(s.hkv), dim3(1024), 0, st, (const float*)scores, s.n, s.keff, sel);
+    const dim3 grid(s.hkv), block(kTopkThreads);
+    const float* sc = scores;
+    if (s.n <= 2 * kTopkThreads) hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, st, sc, s.n, s.keff, sel);
+    else if (s.n <= 8 * kTopkThreads) hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, st, sc, s.n, s.keff, sel);
+    else if (s.n <= 32 * kTopkThreads) hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, st, sc, s.n, s.keff, sel);
+    else hipLaunchKernelGGL(topk_kernel<0>, grid, block, 0, st, sc, s.n, s.keff, sel);
   }
   return hipGetLastError();
 }

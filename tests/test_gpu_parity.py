@@ -141,6 +141,39 @@ def test_deterministic_and_stream(ora):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+# Selection alone at page counts around the top-K kernel's variants: every
+# score held in registers (up to 2048, 8192 and 32768 pages a head) or read
+# again from memory in each radix pass (more pages than that).
+SELECT_ONLY = {
+    "sel-2048": (41, Problem(hq=4, hkv=2, d=64, ps=16, c=16, n=2048, k=64)),
+    "sel-2049-k1": (42, Problem(hq=4, hkv=2, d=64, ps=16, c=16, n=2049, k=1)),
+    "sel-8193-k2048": (43, Problem(hq=4, hkv=2, d=64, ps=16, c=16, n=8193, k=2048)),
+    "sel-32768": (44, Problem(hq=4, hkv=2, d=64, ps=16, c=16, n=32768, k=128)),
+    "sel-40000": (45, Problem(hq=4, hkv=2, d=64, ps=16, c=16, n=40000, k=500)),
+}
+
+
+@pytest.mark.parametrize("name", list(SELECT_ONLY))
+def test_select_page_counts(ora, name):
+    """Rep vectors, scores and the top-K pages against the oracle."""
+    from parity import check_selection
+    seed, p = SELECT_ONLY[name]
+    H.say(f"[select] {name}")
+    x = synth.make_inputs(p, seed)
+    st = H.make_step(p)
+    k = H.dev(x["k_pool"], p.dtype)
+    pt = H.dev(x["page_table"])
+    q = H.dev(x["q"], p.dtype)
+    st.rep_update(k, pt, 0, p.n + p.chunk_pages)
+    st.select(q)
+    torch.cuda.synchronize()
+    orep = ora.rep(p, x["k_pool"], x["page_table"], 0, p.n + p.chunk_pages)
+    oscores = ora.scores(p, ora.qmean(p, x["q"]), orep[: p.n])
+    gscores = st.scores[:, : p.n].cpu().numpy()
+    assert np.max(np.abs(gscores - oscores)) <= 1e-5 * max(1.0, float(np.max(np.abs(oscores))))
+    check_selection(st.sel[:, : p.keff].cpu().numpy(), oscores, p.keff)
+
+
 def test_rep_update_range_only(ora):
     """oomb_rep_update writes exactly rows [first, first + count) of the rep table."""
     seed, p = SMALL["qwen-ps128"]
