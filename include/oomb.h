@@ -32,7 +32,9 @@
  *   - Pointers are DEVICE pointers unless marked host; the caller owns every
  *     buffer.  The library never allocates, frees or synchronises; all work is
  *     enqueued on `stream` (a hipStream_t passed as void*, NULL = the default
- *     stream) and returns before it runs.
+ *     stream) and returns before it runs.  Kernel launches are the only work
+ *     enqueued (no memset or copy), so a caller may capture whole chunk steps
+ *     in a HIP graph; replays produce the same bytes as the eager calls.
  *   - Every device pointer must be 16-byte aligned.
  *   - Element type "T" is the descriptor's dtype (fp32 or bf16); dq, lse, rep,
  *     scores and the gradient pools are always fp32.
