@@ -123,14 +123,31 @@ def run_full(p, seed, ora, report=None, rel_limits=None):
     return report, st, d, x, sel
 
 
-def sample_rows(p, rng, n_extra=12):
-    """Rows t*Hq + g covering the chunk's edges, page edges and every kv-head."""
+ROW_BLOCK = 256   # rows of a kv-head's C*G rows that one forward or dQ workgroup owns
+
+
+def sample_rows(p, rng, n_extra=12, per_block=True):
+    """Rows t*Hq + g covering the chunk's edges, page edges and every kv-head;
+    with per_block, also one random row of every (row block, query head): the
+    row blocks of kv-head h cover its rows t*G + gi (query head h*G + gi) in
+    runs of ROW_BLOCK, and each workgroup writes one such run."""
     toks = {0, 1, p.ps - 1, min(p.ps, p.c - 1), p.c // 2, max(p.c - p.ps - 1, 0), max(p.c - 2, 0), p.c - 1}
     toks |= set(int(t) for t in rng.integers(0, p.c, n_extra))
     rows = []
     for i, t in enumerate(sorted(toks)):
         for g in {(i * 5) % p.hq, (i * 5 + p.group) % p.hq, p.hq - 1 - (i % p.hq)}:
             rows.append(t * p.hq + g)
+    if per_block:
+        G = p.group
+        for b in range((p.c * G + ROW_BLOCK - 1) // ROW_BLOCK):
+            r0, r1 = b * ROW_BLOCK, min((b + 1) * ROW_BLOCK, p.c * G) - 1
+            for gi in range(G):
+                lo, hi = -(-(r0 - gi) // G), (r1 - gi) // G   # tokens t with r0 <= t*G + gi <= r1
+                if lo > hi:
+                    continue
+                t = int(lo + rng.integers(0, hi - lo + 1))
+                for h in range(p.hkv):
+                    rows.append(t * p.hq + h * G + gi)
     return np.array(sorted(set(rows)), dtype=np.int64)
 
 
@@ -237,7 +254,7 @@ def run_sampled(p, seed, ora, report=None, n_local=32, every_row=False):
     odq, _, _ = ora.bwd(p, x["q"], x["k_pool"], x["v_pool"], x["page_table"], sel, x["do"], rows=check, dkdv=False)
     compare(f"dQ[{tag}]", st.dq.cpu().numpy().reshape(-1, p.d)[check], odq, p.dtype, report)
     slot, row = ora.key_slots(p, x["page_table"], sel)
-    model = sum_dk_model(p, x, o_gpu, check, oo, ol, slot, row, rows)
+    model = sum_dk_model(p, x, o_gpu, check, oo, ol, slot, row, rows[:: max(1, len(rows) // 300)])
     del oo, ol, odq
 
     # last chunk tokens: seen only by rows t >= C - n_local

@@ -2,7 +2,8 @@
 
 Small problems: every output element by element (they span several tiles and
 have ragged tails).  Full-size workloads: exact rep vectors and selection,
-O/LSE/dQ on sampled rows (on every row at sparse-256k), the last chunk keys,
+O/LSE/dQ on sampled rows (one in every row block and query head; every row at
+sparse-256k), the last chunk keys,
 invariants, and every key's dK/dV under a dO supported on sampled rows.  Bars:
 see parity.py."""
 import json
