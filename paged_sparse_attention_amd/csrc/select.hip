@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __syncthreads();
   }
   const uint32_t T = prefix;
-  // emit in page order, 1024 pages at a time
+  // emit in page order
   uint32_t out_base = 0, eq_base = 0;
   const uint64_t below = (1ull << lane) - 1ull;
   auto emit = [&](int i, uint32_t key) {
@@ -287,10 +287,78 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __syncthreads();
   };
   if constexpr (R > 0) {
+    // With the keys in registers, two barriers in all: page r*1024 + tid
+    // belongs to group (r, wave), and the groups in (r, wave) order are the
+    // pages in order.  Each wave counts its pages equal to T and above it per
+    // group, wave 0 turns the counts into offsets (where a group's taken
+    // pages start, and how many pages equal to T come before it), then every
+    // thread places its pages.
+    constexpr int Q = R * kTopkWaves;
+    constexpr int E = (Q + 63) / 64;  // groups per lane of wave 0
+    __shared__ uint32_t grp_eq[Q], grp_tk[Q];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (r * kTopkThreads >= n) break;  // uniform
-      emit(r * kTopkThreads + tid, kr[r]);
+      const int i = r * kTopkThreads + tid;
+      const uint64_t bgt = __ballot(i < n && kr[r] > T);
+      const uint64_t beq = __ballot(i < n && kr[r] == T);
+      if (lane == 0) {
+        grp_tk[r * kTopkWaves + wave] = __popcll(bgt);
+        grp_eq[r * kTopkWaves + wave] = __popcll(beq);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t ce[E], cg[E], sum_eq = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int q = lane * E + e;
+        ce[e] = q < Q ? grp_eq[q] : 0u;
+        cg[e] = q < Q ? grp_tk[q] : 0u;
+        sum_eq += ce[e];
+      }
+      uint32_t incl = sum_eq;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      uint32_t eq_off = incl - sum_eq, tk[E], sum_tk = 0, eo[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t room = krem > eq_off ? krem - eq_off : 0u;  // pages equal to T still to take
+        tk[e] = cg[e] + (ce[e] < room ? ce[e] : room);
+        eo[e] = eq_off;
+        eq_off += ce[e];
+        sum_tk += tk[e];
+      }
+      incl = sum_tk;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      uint32_t tk_off = incl - sum_tk;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int q = lane * E + e;
+        if (q < Q) {
+          grp_eq[q] = eo[e];
+          grp_tk[q] = tk_off;
+        }
+        tk_off += tk[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = r * kTopkThreads + tid, q = r * kTopkWaves + wave;
+      const bool gt = i < n && kr[r] > T;
+      const bool eq = i < n && kr[r] == T;
+      const uint64_t beq = __ballot(eq);
+      const bool take = gt || (eq && grp_eq[q] + __popcll(beq & below) < krem);
+      const uint64_t btk = __ballot(take);
+      const uint32_t pos = grp_tk[q] + __popcll(btk & below);
+      if (take && pos < (uint32_t)k) out[pos] = i;
     }
   } else {
     for (int c0 = 0; c0 < n; c0 += kTopkThreads) {
