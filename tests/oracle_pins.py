@@ -433,6 +433,29 @@ def pin_bwd_invariants(ora):
         close(dv[h].sum(axis=0), x["do"][:, h * G:(h + 1) * G].sum(axis=(0, 1)), 1e-12, "sum dV")
 
 
+def pin_bwd_constant_values(ora):
+    """Every value vector of a kv-head equal to one vector v_h: each row's
+    output is v_h whatever the weights, so dO . V_j equals Dt = dO . O for
+    every visible key j, every dS is zero, and with it dQ and dK; dV_j is then
+    the sum over rows of P_rj dO_r, whose sum over keys is the sum of dO."""
+    p, x = tiny(hq=4, hkv=2, n=8, k=3, c=8, ps=4, d=8)
+    rng = np.random.default_rng(5)
+    vh = rng.normal(size=(p.hkv, p.d))
+    v = np.empty_like(x["v_pool"])
+    for h in range(p.hkv):
+        v[:, h] = vh[h]
+    sel, _ = ora.selection(p, x["q"], x["k_pool"], x["page_table"])
+    o, _ = ora.fwd(p, x["q"], x["k_pool"], v, x["page_table"], sel)
+    G = p.group
+    want_o = np.stack([vh[g // G] for _ in range(p.c) for g in range(p.hq)])
+    close(o, want_o, 1e-13, "O = v")
+    dq, dk, dv = ora.bwd(p, x["q"], x["k_pool"], v, x["page_table"], sel, x["do"])
+    close(dq, np.zeros_like(dq), 1e-13, "dQ = 0")
+    close(dk, np.zeros_like(dk), 1e-13, "dK = 0")
+    for h in range(p.hkv):
+        close(dv[h].sum(axis=0), x["do"][:, h * G:(h + 1) * G].sum(axis=(0, 1)), 1e-12, "sum dV")
+
+
 def pin_bwd_linearity(ora):
     """Gradients are linear in dO."""
     p, x = tiny(hq=4, hkv=2, n=6, k=2)
