@@ -64,16 +64,19 @@ def touched_mask(p, ora, pt, sel):
     return m
 
 
-def run_full(p, seed, ora, report=None, rel_limits=None):
+def run_full(p, seed, ora, report=None, rel_limits=None, tweak=None):
     """Every output against the oracle, element by element (small problems).
     rel_limits: {output name: r} replaces the official max-abs bar of that
-    output by r * max |reference| (a documented known limit only)."""
+    output by r * max |reference| (a documented known limit only).  tweak(x),
+    if given, edits the generated inputs in place before both sides see them."""
     rel_limits = rel_limits or {}
 
     def bar(name, want):
         return rel_limits[name] * float(np.max(np.abs(want))) if name in rel_limits else None
     report = {} if report is None else report
     x = synth.make_inputs(p, seed)
+    if tweak is not None:
+        tweak(x)
     d = Device(p, x, canary_seed=seed)
     st = make_step(p)
     pages = p.n + p.chunk_pages

@@ -16,6 +16,7 @@ import torch
 import synth
 from synth import Problem, WORKLOADS
 import gpu_harness as H
+from parity import ZERO_REF
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +85,32 @@ def test_small_elementwise(ora, name):
     H.say(f"case {name}: {p}")
     report, *_ = H.run_full(p, seed, ora)
     H.say(f"  {json.dumps(report, default=float)}")
+    _save(name, report)
+
+
+# Every value vector of a kv-head set to that head's first stored value row:
+# O is that vector on every row and dQ = dK = 0 exactly (dO . V_j equals
+# Dt = dO . O for every key), so the kernels' Dt and dS must cancel to within
+# their rounding.
+CONST_V = {
+    "const-v-bf16": (51, Problem(hq=28, hkv=4, d=128, ps=128, c=256, n=12, k=4)),
+    "const-v-fp32": (52, Problem(hq=4, hkv=2, d=64, ps=16, c=64, n=9, k=3, dtype="f32")),
+}
+
+
+@pytest.mark.parametrize("name", list(CONST_V))
+def test_constant_values(ora, name):
+    seed, p = CONST_V[name]
+    H.say(f"case {name}: {p}")
+
+    def tweak(x):
+        v = x["v_pool"]
+        v[...] = v[:1, :, :1, :]   # [slots][hkv][ps][d]: slot 0, row 0 of each head everywhere
+
+    report, st, d, x, sel = H.run_full(p, seed, ora, tweak=tweak)
+    H.say(f"  {json.dumps(report, default=float)}")
+    # the oracle's dQ and dK are zero up to fp64 rounding, so only the absolute bar applied to them
+    assert report["dQ"]["rms_ref"] <= ZERO_REF and report["dK"]["rms_ref"] <= ZERO_REF, report
     _save(name, report)
 
 
