@@ -98,6 +98,27 @@ CONST_V = {
 }
 
 
+# Q = 0: every score of a row is 0, so the weights are uniform over its visible
+# keys (ties everywhere for the running maximum) and O is their mean value.
+ZERO_Q = {
+    "zero-q-bf16": (53, Problem(hq=28, hkv=4, d=128, ps=128, c=256, n=12, k=4)),
+    "zero-q-fp32": (54, Problem(hq=4, hkv=2, d=64, ps=16, c=64, n=9, k=3, dtype="f32")),
+}
+
+
+@pytest.mark.parametrize("name", list(ZERO_Q))
+def test_zero_queries(ora, name):
+    seed, p = ZERO_Q[name]
+    H.say(f"case {name}: {p}")
+
+    def tweak(x):
+        x["q"][...] = 0
+
+    report, *_ = H.run_full(p, seed, ora, tweak=tweak)
+    H.say(f"  {json.dumps(report, default=float)}")
+    _save(name, report)
+
+
 @pytest.mark.parametrize("name", list(CONST_V))
 def test_constant_values(ora, name):
     seed, p = CONST_V[name]
