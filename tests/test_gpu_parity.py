@@ -119,6 +119,37 @@ def test_zero_queries(ora, name):
     _save(name, report)
 
 
+# Scores that rise along the key list: every query has a component a along one
+# unit vector u and key j one of B * j / J, so a row's largest score grows by
+# about B (in natural-log units) from the first key to the last and the
+# forward's running maximum moves up tile after tile, past its rescaling slack
+# several times, instead of settling in the first tiles as with random data.
+RISING = (55, Problem(hq=7, hkv=1, d=128, ps=64, c=128, n=32, k=32), 14.0)
+
+
+def test_rising_scores(ora):
+    seed, p, B = RISING
+    H.say(f"case rising-scores: {p}, B {B}")
+    rng = np.random.default_rng(seed)
+    u = rng.normal(size=p.d)
+    u /= np.linalg.norm(u)
+    nkeys = p.n * p.ps + p.c
+
+    def tweak(x):
+        pt = x["page_table"]
+        k = synth.as_float(x["k_pool"], p.dtype)
+        for m in range(p.n + p.chunk_pages):   # logical page m holds key positions m*ps .. m*ps+ps-1
+            j = m * p.ps + np.arange(p.ps)
+            k[pt[m]] += (B * j / nkeys)[None, :, None] * u
+        x["k_pool"][...] = synth.bf16_bits(k)
+        q = synth.as_float(x["q"], p.dtype) + np.sqrt(p.d) * u
+        x["q"][...] = synth.bf16_bits(q)
+
+    report, *_ = H.run_full(p, seed, ora, tweak=tweak)
+    H.say(f"  {json.dumps(report, default=float)}")
+    _save("rising-scores", report)
+
+
 @pytest.mark.parametrize("name", list(CONST_V))
 def test_constant_values(ora, name):
     seed, p = CONST_V[name]
