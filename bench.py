@@ -502,7 +502,7 @@ def sequence_bench(args):
         "config": {"workload": args.sequence, "n_q_heads": s.hq, "n_kv_heads": s.hkv, "head_dim": s.d,
                    "page_size": s.ps, "chunk_len": s.c, "chunks": s.chunks, "tokens": tokens, "top_k": s.k,
                    "initial_pages": s.n0, "visible_pairs": s.pairs(), "seed": seed,
-                   "activations": "one chunk, forward re-run in the backward" if args.recompute else "every chunk kept",
+                   "activations": "two chunks' buffers, forward re-run alongside the next chunk's backward" if args.recompute else "every chunk kept",
                    "kv_cache": "pinned host memory, staged per chunk" if args.offload else "device"},
         "roofline": {"bound": "mfma", "kernel": "whole pass (every kernel of every chunk)", "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,

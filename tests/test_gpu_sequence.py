@@ -4,9 +4,10 @@ called chunk by chunk) against the whole-sequence oracle, element by element.
 Per chunk: the selected pages (identical, or inside the near-tie band), O, LSE
 and dQ; for the whole sequence: the dK/dV pools, which every chunk's backward
 adds into (compared as pool after minus the seeded prefill).  The driver's
-recompute mode (one activation buffer, the forward re-run in the backward with
-the saved selection) must give bitwise the results of the mode that keeps every
-chunk's O and LSE."""
+recompute modes (the forward re-run in the backward with the saved selection:
+serially with one activation buffer, or on a second stream alongside the next
+chunk's backward with two) must give bitwise the results of the mode that keeps
+every chunk's O and LSE."""
 from __future__ import annotations
 
 import json
@@ -36,7 +37,7 @@ def _gpu():
         pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
 
 
-def run_sequence(s, seed, keep=True, raw=None):
+def run_sequence(s, seed, keep=True, raw=None, overlap=True):
     """Forward and backward over the sequence.  raw, if a dict, receives every
     chunk's O and LSE (copied as the forward produces them) and the pools."""
     from paged_sparse_attention_amd.sequence import ChunkedSequence
@@ -47,7 +48,7 @@ def run_sequence(s, seed, keep=True, raw=None):
     dk0, dv0 = synth.canary(last, seed, "k"), synth.canary(last, seed, "v")
     dk, dv = H.dev(dk0), H.dev(dv0)
     drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
-                          softmax_scale=s.scale, keep_activations=keep)
+                          softmax_scale=s.scale, keep_activations=keep, overlap_recompute=overlap)
     outs = []
     drv.forward(q, k, v, pt, on_chunk=lambda i, o, lse: outs.append((o.clone(), lse.clone())))
     drv.backward(q, k, v, pt, do, dk, dv)
@@ -88,14 +89,17 @@ def test_sequence_elementwise(ora, name):
 def test_recompute_matches_kept_activations(name):
     seed, s = SEQ[name]
     H.say(f"case {name} recompute: {s}")
-    kept, redo = {}, {}
+    kept = {}
     _, a, _, _ = run_sequence(s, seed, keep=True, raw=kept)
-    _, b, _, _ = run_sequence(s, seed, keep=False, raw=redo)
-    assert b.o.shape[0] == 1 and b.lse.shape[0] == 1     # one chunk's activations only
-    for i in range(s.chunks):
-        assert torch.equal(a.sel[i], b.sel[i]), f"chunk {i} selection"
-        assert torch.equal(kept["o"][i], redo["o"][i]), f"chunk {i} O"
-        assert torch.equal(kept["o"][i], a.o[i]), f"chunk {i} O handed to the callback"
-        assert torch.equal(kept["lse"][i], redo["lse"][i]), f"chunk {i} LSE"
-        assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ"
-    assert torch.equal(kept["dk"], redo["dk"]) and torch.equal(kept["dv"], redo["dv"]), "dK/dV pools"
+    for overlap, nbuf in ((False, 1), (True, 2)):
+        redo = {}
+        _, b, _, _ = run_sequence(s, seed, keep=False, raw=redo, overlap=overlap)
+        assert b.o.shape[0] == nbuf and b.lse.shape[0] == nbuf     # activations of one or two chunks only
+        for i in range(s.chunks):
+            assert torch.equal(a.sel[i], b.sel[i]), f"chunk {i} selection"
+            assert torch.equal(kept["o"][i], redo["o"][i]), f"chunk {i} O"
+            assert torch.equal(kept["o"][i], a.o[i]), f"chunk {i} O handed to the callback"
+            assert torch.equal(kept["lse"][i], redo["lse"][i]), f"chunk {i} LSE"
+            assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ (overlap {overlap})"
+        assert torch.equal(kept["dk"], redo["dk"]) and torch.equal(kept["dv"], redo["dv"]), \
+            f"dK/dV pools (overlap {overlap})"
