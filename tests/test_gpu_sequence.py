@@ -37,7 +37,7 @@ def _gpu():
         pytest.fail("no GPU visible: the -m gpu tests need an MI355X")
 
 
-def run_sequence(s, seed, keep=True, raw=None, overlap=True):
+def run_sequence(s, seed, keep=True, raw=None, overlap=True, stream=None):
     """Forward and backward over the sequence.  raw, if a dict, receives every
     chunk's O and LSE (copied as the forward produces them) and the pools."""
     from paged_sparse_attention_amd.sequence import ChunkedSequence
@@ -50,8 +50,11 @@ def run_sequence(s, seed, keep=True, raw=None, overlap=True):
     drv = ChunkedSequence(s.hq, s.hkv, s.d, s.ps, s.c, s.chunks, s.k, n_initial_pages=s.n0, dtype=s.dtype,
                           softmax_scale=s.scale, keep_activations=keep, overlap_recompute=overlap)
     outs = []
-    drv.forward(q, k, v, pt, on_chunk=lambda i, o, lse: outs.append((o.clone(), lse.clone())))
-    drv.backward(q, k, v, pt, do, dk, dv)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        drv.forward(q, k, v, pt, stream=stream, on_chunk=lambda i, o, lse: outs.append((o.clone(), lse.clone())))
+        drv.backward(q, k, v, pt, do, dk, dv, stream=stream)
     torch.cuda.synchronize()
     if raw is not None:
         raw.update(o=[o for o, _ in outs], lse=[l for _, l in outs], dk=dk, dv=dv)
@@ -103,3 +106,17 @@ def test_recompute_matches_kept_activations(name):
             assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ (overlap {overlap})"
         assert torch.equal(kept["dk"], redo["dk"]) and torch.equal(kept["dv"], redo["dv"]), \
             f"dK/dV pools (overlap {overlap})"
+
+
+def test_overlapped_recompute_on_a_caller_stream():
+    """The overlapped re-run backward ordered on a stream the caller passes
+    (not the default one) gives bitwise the results of kept activations."""
+    seed, s = SEQ["seq-qwen-shape"]
+    H.say("case seq-qwen-shape, recompute on a caller stream")
+    kept, redo = {}, {}
+    _, a, _, _ = run_sequence(s, seed, keep=True, raw=kept)
+    _, b, _, _ = run_sequence(s, seed, keep=False, raw=redo, overlap=True, stream=torch.cuda.Stream())
+    for i in range(s.chunks):
+        assert torch.equal(kept["o"][i], redo["o"][i]), f"chunk {i} O"
+        assert torch.equal(a.dq[i], b.dq[i]), f"chunk {i} dQ"
+    assert torch.equal(kept["dk"], redo["dk"]) and torch.equal(kept["dv"], redo["dv"]), "dK/dV pools"
