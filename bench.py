@@ -333,6 +333,18 @@ def layer_bench(args):
 
     seed, s = synth.LAYERS[args.layer]
     print(f"bench: layer {args.layer} {s}", file=sys.stderr, flush=True)
+    # GEMM solutions: hipBLASLt/rocBLAS defaults, or a TunableOp table of the
+    # layer's GEMM shapes tuned once on an MI355X (read only: nothing is tuned
+    # or written here; its validators reject it under other library versions)
+    gemm = "hipBLASLt/rocBLAS defaults"
+    if args.gemm_table != "none":
+        import tempfile
+        torch.cuda.tunable.set_filename(os.path.join(tempfile.gettempdir(), "oomb_tunableop.csv"))
+        torch.cuda.tunable.tuning_enable(False)
+        torch.cuda.tunable.enable(True)
+        ok = torch.cuda.tunable.read_file(args.gemm_table)
+        gemm = "TunableOp table %s%s" % (os.path.relpath(args.gemm_table, ROOT), "" if ok else " (rejected: defaults used)")
+    print(f"bench: GEMM selection: {gemm}", file=sys.stderr, flush=True)
     bits = synth.make_layer_inputs(s, seed)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
     x, dy = dev(bits["x"]), dev(bits["dy"]).float()
@@ -391,7 +403,7 @@ def layer_bench(args):
         "config": {"workload": args.layer, "hidden": s.hidden, "n_q_heads": s.hq, "n_kv_heads": s.hkv,
                    "head_dim": s.d, "intermediate": s.inter, "page_size": s.ps, "chunk_len": s.c,
                    "chunks": s.chunks, "tokens": tokens, "top_k": s.k, "seed": seed,
-                   "activations": "one chunk, forward re-run in the backward"},
+                   "activations": "one chunk, forward re-run in the backward", "gemm_selection": gemm},
         "gemm_tflops": gemm_flops / ((ms - attn) / 1e3) / 1e12,
         "attention_tflops": 14.0 * s.d * pairs / (attn / 1e3) / 1e12,
         # peak = what is held before the pass (inputs, layer) + the pass's
@@ -529,6 +541,8 @@ def main():
     ap.add_argument("--layer", default=None, metavar="NAME",
                     help="instead of one chunk step, time a decoder layer with random weights around the path, "
                          "chunk by chunk, forward and backward (synth.LAYERS, e.g. layer-qwen-64k)")
+    ap.add_argument("--gemm-table", default=os.path.join(ROOT, "paged_sparse_attention_amd", "tunableop_gfx950.csv"),
+                    help="--layer: TunableOp table of the layer's GEMM shapes (read only), or 'none' for the defaults")
     ap.add_argument("--recompute", action="store_true",
                     help="with --sequence: keep one chunk's O/LSE and re-run each chunk's forward in the backward "
                          "(14*D flop per pair are still credited; the re-run forward is extra work)")
